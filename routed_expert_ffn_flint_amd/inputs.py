@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the Flint MoE layer.
+
+This module only draws random numbers.  It holds none of the layer's
+arithmetic: the GPU path and the CPU oracle both take what it returns as input.
+
+Workloads (sizes from the Flint pages' layer shape: hidden 2048, 256 routed
+experts, top-6, expert width 512, shared width 1024; no trained weights exist
+here, so every tensor is drawn):
+
+  toy          T=64,    H=256,  E=16,  K=2, I=64,  Is=128,  float32,  seed 0
+  decode32     T=32,    H=2048, E=256, K=6, I=512, Is=1024, bf16,     seed 0
+  prefill4096  T=4096,  same layer, no router bias,                   seed 0
+  skew16384    T=16384, same layer, Zipf(1.1) per-expert router bias, seed 0
+  stack47      T=256,   47 distinct layers, RMSNorm between layers,   seed 1
+
+Weights ~ N(0, 0.02^2), hidden states ~ N(0, 1), drawn in float32 and rounded
+to bf16 (round-to-nearest-even, torch's conversion) for the bf16 workloads.
+
+Each tensor has its own generator, seeded from (seed, layer, tensor id), so a
+layer can be drawn without drawing the ones before it, and a tensor can be
+drawn on the CPU or directly on the GPU (the two devices' generators give
+different, equally valid, streams; a test always hands the same drawn values
+to both sides).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    hidden: int
+    n_experts: int
+    top_k: int
+    inter: int
+    shared_inter: int
+    bf16: bool
+    seed: int
+    zipf_bias: bool = False
+    layers: int = 1
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.bf16 else torch.float32
+
+
+WORKLOADS = {
+    "toy": Workload("toy", 64, 256, 16, 2, 64, 128, False, 0),
+    "decode32": Workload("decode32", 32, 2048, 256, 6, 512, 1024, True, 0),
+    "prefill4096": Workload("prefill4096", 4096, 2048, 256, 6, 512, 1024, True, 0),
+    "skew16384": Workload("skew16384", 16384, 2048, 256, 6, 512, 1024, True, 0, zipf_bias=True),
+    "stack47": Workload("stack47", 256, 2048, 256, 6, 512, 1024, True, 1, layers=47),
+}
+
+WEIGHT_STD = 0.02
+ZIPF_S = 1.1
+ZIPF_SCALE = 0.5
+
+_TENSOR_IDS = {"router": 1, "bias": 2, "gate": 3, "up": 4, "down": 5,
+               "shared_gate": 6, "shared_up": 7, "shared_down": 8, "x": 9}
+
+
+def _gen(seed: int, layer: int, tensor: str, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + layer * 7919 + _TENSOR_IDS[tensor] * 104_729) % (2**62))
+    return g
+
+
+def _normal(shape, std, dtype, seed, layer, tensor, device):
+    dev = torch.device(device)
+    g = _gen(seed, layer, tensor, dev)
+    if dtype == torch.float32:
+        t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        return t.mul_(std) if std != 1.0 else t
+    # Draw in float32 chunks and round, to bound the float32 temporary.
+    out = torch.empty(shape, device=dev, dtype=dtype)
+    flat = out.view(-1)
+    chunk = 1 << 26
+    for s in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - s)
+        t = torch.randn((n,), generator=g, device=dev, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        flat[s:s + n].copy_(t)
+    return out
+
+
+def zipf_bias(n_experts: int, seed: int) -> np.ndarray:
+    """Per-expert router bias that skews the load: expert e gets rank r(e) from a
+    seeded permutation of 1..E and bias 0.5 * ln(E * p_r), p_r = r^-1.1 / sum_j j^-1.1."""
+    g = torch.Generator().manual_seed(seed * 31 + 7)
+    ranks = torch.randperm(n_experts, generator=g).numpy() + 1
+    j = np.arange(1, n_experts + 1, dtype=np.float64)
+    p = ranks.astype(np.float64) ** (-ZIPF_S) / np.sum(j ** (-ZIPF_S))
+    return (ZIPF_SCALE * np.log(n_experts * p)).astype(np.float32)
+
+
+def make_layer(wl: Workload, layer: int = 0, device="cpu", with_shared: bool = True) -> dict:
+    """Weights of one layer as torch tensors on ``device``.
+
+    Layouts (row-major, reduction dimension contiguous):
+      router [E,H], bias [E] float32 or None, gate/up [E,I,H], down [E,H,I],
+      shared_gate/shared_up [Is,H], shared_down [H,Is].
+    """
+    E, H, I, Is = wl.n_experts, wl.hidden, wl.inter, wl.shared_inter
+    dt, s = wl.torch_dtype, wl.seed
+    w = {
+        "router": _normal((E, H), WEIGHT_STD, dt, s, layer, "router", device),
+        "gate": _normal((E, I, H), WEIGHT_STD, dt, s, layer, "gate", device),
+        "up": _normal((E, I, H), WEIGHT_STD, dt, s, layer, "up", device),
+        "down": _normal((E, H, I), WEIGHT_STD, dt, s, layer, "down", device),
+        "bias": None,
+    }
+    if wl.zipf_bias:
+        w["bias"] = torch.from_numpy(zipf_bias(E, s)).to(device)
+    if with_shared and Is > 0:
+        w["shared_gate"] = _normal((Is, H), WEIGHT_STD, dt, s, layer, "shared_gate", device)
+        w["shared_up"] = _normal((Is, H), WEIGHT_STD, dt, s, layer, "shared_up", device)
+        w["shared_down"] = _normal((H, Is), WEIGHT_STD, dt, s, layer, "shared_down", device)
+    return w
+
+
+def make_tokens(wl: Workload, T: int | None = None, device="cpu", stream: int = 0) -> torch.Tensor:
+    """Hidden states x [T,H] ~ N(0,1) in the workload's dtype."""
+    T = wl.T if T is None else T
+    return _normal((T, wl.hidden), 1.0, wl.torch_dtype, wl.seed, 10**6 + stream, "x", device)
+
+
+def custom(name="custom", T=8, hidden=64, n_experts=8, top_k=2, inter=64, shared_inter=64,
+           bf16=True, seed=0, zipf=False, layers=1) -> Workload:
+    return Workload(name, T, hidden, n_experts, top_k, inter, shared_inter, bf16, seed, zipf, layers)
+
+
+def expected_distinct_experts(T: int, E: int = 256, K: int = 6) -> float:
+    """Expected number of experts hit by T tokens under uniform routing (a sizing
+    aid for the roofline figures; the benchmark uses the measured count)."""
+    return E * (1.0 - (1.0 - K / E) ** T) if T > 0 else 0.0
+
+
+def to_numpy_f32(t: torch.Tensor | None):
+    """Exact float32 copy of a (bf16 or float32) tensor, on the host."""
+    if t is None:
+        return None
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+__all__ = ["Workload", "WORKLOADS", "make_layer", "make_tokens", "zipf_bias", "custom",
+           "expected_distinct_experts", "to_numpy_f32"]
