@@ -1,0 +1,314 @@
+"""Benchmark of the Flint MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode32|prefill4096|skew16384|stack47|toy]
+
+A step is one pass of the whole layer (router, top-k, dispatch, gate/up +
+SwiGLU, down, combine; for stack47 all 47 layers with RMSNorm between them) over
+one batch of tokens whose inputs and weights are resident in HBM.  The default
+workload is the decode batch: one Flint-shaped layer (H=2048, 256 experts,
+top-6, expert width 512, shared width 1024, bf16) on T=32 tokens.  Single-layer
+workloads rotate through several independently drawn weight copies so that the
+last-level cache cannot serve repeated weight reads.
+
+Prints ONE JSON line.  Beside the headline throughput:
+  roofline      the dominant kernel's algorithmic bytes (or flops) per launch
+                over its mean launch duration, from HIP events recorded around
+                it on the library's stream during a second pass of the same
+                steps, against MI355X's published peak;
+  cpu_baseline  the oracle (plain fp64 C) timed on the host on a bounded
+                sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s (bf16, H=2048, 256e top-6) + % HBM/MFMA roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode32")
+    p.add_argument("--copies", type=int, default=4, help="weight copies rotated (single-layer workloads)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true", help="replay the steps from a captured HIP graph")
+    return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(ev)
+        return out
+
+    def ms(self, a, b):
+        v = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(v), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return v.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def algorithmic(wl, idx_np):
+    """Algorithmic HBM bytes and flops of one layer call, per stage.
+
+    Weights count once per distinct expert the batch selects; activations are
+    read once; outputs written once (float32 out)."""
+    T, H, E, K, I, Is = wl.T, wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter
+    eb = 2 if wl.bf16 else 4
+    distinct = len(np.unique(idx_np))
+    gate_up_bytes = distinct * 2 * I * H * eb + 2 * Is * H * eb + T * H * eb + (T * K * I + T * Is) * eb
+    down_bytes = distinct * H * I * eb + Is * H * eb + (T * K * I + T * Is) * eb + (T * K + T) * H * 4
+    router_bytes = E * H * eb + T * H * eb
+    layer_bytes = (E * H + distinct * 3 * I * H + 3 * Is * H) * eb + T * H * eb + T * H * 4
+    flops = {
+        "router": 2 * T * E * H,
+        "gate_up": 4 * T * K * I * H + 4 * T * Is * H,
+        "down": 2 * T * K * I * H + 2 * T * Is * H,
+    }
+    flops["layer"] = flops["router"] + flops["gate_up"] + flops["down"]
+    return {"distinct": distinct, "gate_up_bytes": gate_up_bytes, "down_bytes": down_bytes,
+            "router_bytes": router_bytes, "layer_bytes": layer_bytes, "flops": flops}
+
+
+def cpu_baseline(wl, w_dev, x_dev, target_s):
+    """The oracle on the host: whole-layer forward of the workload's first
+    tokens, repeated until about target_s seconds of work."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import oracle as orc
+    from routed_expert_ffn_flint_amd import inputs
+
+    o = orc.default()
+    d = orc.dims(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, wl.bf16)
+    wh = {k: inputs.to_numpy_f32(v) for k, v in w_dev.items()}
+    n_tok = min(wl.T, 32)
+    xh = inputs.to_numpy_f32(x_dev[:n_tok])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o.forward(d, xh, wh)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": o.threads(), "kind": "oracle",
+            "sample": f"{wl.name} layer (weight copy 0), the first {n_tok} tokens, whole-layer forward "
+                      f"in fp64, repeated {reps}x over {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    import torch
+
+    from routed_expert_ffn_flint_amd import _lib, api, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    lib = _lib.load()
+    wl = inputs.WORKLOADS[args.workload]
+    d = api.dims_of(wl)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    stack = wl.layers > 1
+    n_copies = wl.layers if stack else max(1, args.copies)
+    layers = [inputs.make_layer(wl, c, dev) for c in range(n_copies)]
+    wstructs = [api.weights_struct(d, w) for w in layers]
+    x = inputs.make_tokens(wl, device=dev)
+    T = wl.T
+    ws = api.workspace(d, T, dev)
+    out = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, wl.top_k), dtype=torch.float32, device=dev)
+    xs = [torch.empty((T, wl.hidden), dtype=torch.bfloat16, device=dev) for _ in range(2)] if stack else None
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    dref = ctypes.byref(d)
+    wsp, wsn = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    outp, idxp, twp = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(tw.data_ptr())
+    xp = ctypes.c_void_p(x.data_ptr())
+
+    def layer_call(c, xin, events=None):
+        if events is None:
+            st = lib.flint_moe_forward(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp, wsp, wsn, sp)
+        else:
+            arr = (ctypes.c_void_p * 6)(*[e.value for e in events])
+            st = lib.flint_moe_forward_profiled(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp,
+                                                wsp, wsn, sp, arr)
+        if st != 0:
+            raise api.FlintError(st, "flint_moe_forward")
+
+    def step(i, events=None):
+        if not stack:
+            layer_call(i % n_copies, xp, events[0] if events else None)
+            return
+        xin = xp
+        for l in range(n_copies):
+            layer_call(l, xin, events[l] if events else None)
+            if l + 1 < n_copies:
+                nxt = xs[l % 2]
+                st = lib.flint_rmsnorm(T, wl.hidden, outp, ctypes.c_void_p(nxt.data_ptr()), 1e-6, sp)
+                if st != 0:
+                    raise api.FlintError(st, "flint_rmsnorm")
+                xin = ctypes.c_void_p(nxt.data_ptr())
+
+    # routing per copy (for the algorithmic byte counts)
+    per_copy = []
+    if stack:
+        step(0)
+    for c in range(n_copies if not stack else 1):
+        layer_call(c, xp)
+        torch.cuda.synchronize()
+        per_copy.append(algorithmic(wl, idx.cpu().numpy()))
+    if stack:
+        # algorithmic bytes of the stack: every layer's own routing
+        per_copy = []
+        xin = xp
+        for l in range(n_copies):
+            layer_call(l, xin)
+            torch.cuda.synchronize()
+            per_copy.append(algorithmic(wl, idx.cpu().numpy()))
+            if l + 1 < n_copies:
+                nxt = xs[l % 2]
+                lib.flint_rmsnorm(T, wl.hidden, outp, ctypes.c_void_p(nxt.data_ptr()), 1e-6, sp)
+                xin = ctypes.c_void_p(nxt.data_ptr())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        # one graph holding n_copies consecutive steps (one full weight rotation)
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            sp = ctypes.c_void_p(s2.cuda_stream)
+            with torch.cuda.graph(g, stream=s2):
+                for i in range(n_copies if not stack else 1):
+                    step(i)
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        graph = g
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- headline: K steps, bracketed by synchronisation -------------------
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    if graph is not None:
+        per = n_copies if not stack else 1
+        reps = max(1, args.steps // per)
+        for _ in range(reps):
+            graph.replay()
+        steps_done = reps * per
+    else:
+        for i in range(args.steps):
+            step(i)
+        steps_done = args.steps
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / steps_done
+    tokens_per_s = T / (ms / 1e3)
+
+    # ---- per-stage timing pass (events on the library's stream) -------------
+    hev = HipEvents()
+    n_prof = min(args.steps, 100)
+    n_layers_step = n_copies if stack else 1
+    ev_sets = [[hev.create(6) for _ in range(n_layers_step)] for _ in range(n_prof)]
+    for i in range(n_prof):
+        step(i, ev_sets[i])
+    torch.cuda.synchronize()
+    names = ["router", "topk_dispatch", "gate_up", "down", "combine"]
+    stage = {n: [] for n in names}
+    for i in range(n_prof):
+        for evs in ev_sets[i]:
+            for j, n in enumerate(names):
+                stage[n].append(hev.ms(evs[j], evs[j + 1]))
+    for sets in ev_sets:
+        for evs in sets:
+            hev.destroy(evs)
+    stage_us = {n: float(np.mean(v) * 1e3) for n, v in stage.items()}
+
+    # algorithmic figures averaged over the copies the steps used
+    avg = lambda key: float(np.mean([p[key] for p in per_copy]))  # noqa: E731
+    gate_up_bytes = avg("gate_up_bytes")
+    layer_bytes = avg("layer_bytes")
+    layer_flops = float(np.mean([p["flops"]["layer"] for p in per_copy]))
+    gu_flops = float(np.mean([p["flops"]["gate_up"] for p in per_copy]))
+    big = T >= 2048
+    if big:
+        achieved = gu_flops / (stage_us["gate_up"] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "k_gate_up (grouped gate/up GEMM + SwiGLU)",
+                    "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                    "per_launch": {"flops": gu_flops, "mean_us": stage_us["gate_up"]}}
+    else:
+        achieved = gate_up_bytes / (stage_us["gate_up"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "k_gate_up (grouped gate/up GEMM + SwiGLU)",
+                    "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "per_launch": {"bytes": gate_up_bytes, "mean_us": stage_us["gate_up"]}}
+    layer_time_s = ms / 1e3 / (n_copies if stack else 1)
+    layer = {"hbm_GBs": layer_bytes / layer_time_s / 1e9,
+             "hbm_frac": layer_bytes / layer_time_s / 1e9 / HBM_PEAK_GBS,
+             "mfma_TFLOPs": layer_flops / layer_time_s / 1e12,
+             "mfma_frac": layer_flops / layer_time_s / 1e12 / BF16_PEAK_TFLOPS,
+             "algorithmic_bytes": layer_bytes, "flops": layer_flops,
+             "distinct_experts": avg("distinct")}
+
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps_done, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {'47 stacked' if stack else 'one'} Flint MoE layer(s), T={T}, "
+                               f"H={wl.hidden}, E={wl.n_experts} top-{wl.top_k}, I={wl.inter}, "
+                               f"Is={wl.shared_inter}", "T": T, "weight_copies": n_copies,
+                   "graph": bool(graph is not None), "wall_s": wall},
+        "roofline": roofline,
+        "layer_roofline": layer,
+        "stages_us": stage_us,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, layers[0], x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

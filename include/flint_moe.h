@@ -1,0 +1,171 @@
+/*
+ * flint_moe.h -- C ABI of the Flint routed-expert MoE layer for AMD MI355X (gfx950).
+ *
+ * The layer (pages on the Flint release):
+ *   - "Recursive Flint serving kit" review (asivanadi0.github.io), section
+ *     "The architecture, from the config": 256 routed experts per MoE layer,
+ *     6 selected per token, plus an always-on shared expert; expert intermediate
+ *     size 512, shared expert 1024; sigmoid router scores with normalised top-k,
+ *     not softmax.  The same section's parameter count fits gated three-matrix
+ *     (gate, up, down) experts.
+ *   - "Recursive opens Flint, a 40B coding model with 2.5B active" (promtime.net),
+ *     section "What runs on each token": a router picks 6 of 256 expert
+ *     sub-networks for each token and one shared expert runs every time.
+ *
+ * For each token x (length H):
+ *   z_e   = x . router[e] (+ router_bias[e])            e = 0..E-1, float32
+ *   s_e   = sigmoid(z_e)                                 float32
+ *   S     = the K experts with the largest s_e (equal scores: lower index first),
+ *           reported in ascending expert order
+ *   w_e   = s_e / sum_{j in S} s_j                       float32, e in S
+ *   h_e   = silu(gate[e] x) * (up[e] x),  silu(g) = g * sigmoid(g), stored in the
+ *           layer's dtype
+ *   out   = sum_{e in S} w_e * down[e] h_e  +  shared_down (silu(shared_gate x) * (shared_up x))
+ *
+ * Conventions (all entry points):
+ *   - Every pointer except `dims`/`weights` structs is a DEVICE pointer owned by
+ *     the caller (for example the storage of a torch tensor).  The library never
+ *     allocates, frees or synchronises; it enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream) and returns.
+ *   - Layouts are row-major with the reduction dimension contiguous:
+ *       x [T][H]; router [E][H]; router_bias [E] float32 or NULL;
+ *       gate, up [E][I][H]; down [E][H][I];
+ *       shared_gate, shared_up [Is][H]; shared_down [H][Is].
+ *     Element type of x and of every weight except router_bias: dims.dtype.
+ *   - Supported set (anything else is refused with FLINT_UNSUPPORTED, never
+ *     served by a fallback -- the serving-kit review, section "What isn't
+ *     validated, and what the kit refuses to do", praises refusing unsupported
+ *     configurations loudly rather than running a path that ignores the sigmoid
+ *     routing):
+ *       dtype F32 or BF16; 1 <= K <= 8; K <= E <= 256; H, I, Is multiples of 64
+ *       (Is = 0 means no shared expert); H <= 8192; I, Is <= 4096;
+ *       T * K < 2^31; every device pointer 16-byte aligned.
+ *   - T = 0 is a valid no-op.  T < 0 or a NULL required pointer is
+ *     FLINT_INVALID_ARG.  Argument errors are detected on the host before any
+ *     launch and leave every output untouched.  FLINT_DEVICE_ERROR reports an
+ *     immediate launch failure; faults during execution surface at the
+ *     caller's next synchronisation.
+ *   - Non-finite inputs give undefined results.
+ *   - The calls keep no state between calls and may be issued from several
+ *     threads on different streams, each with its own workspace.
+ */
+#ifndef FLINT_MOE_H
+#define FLINT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t flint_status;
+#define FLINT_OK 0
+#define FLINT_INVALID_ARG 1
+#define FLINT_UNSUPPORTED 2
+#define FLINT_WORKSPACE_TOO_SMALL 3
+#define FLINT_DEVICE_ERROR 4
+
+typedef int32_t flint_dtype;
+#define FLINT_F32 0
+#define FLINT_BF16 1
+
+/* Layer shape: hidden size H, routed experts E, experts per token K, routed
+ * expert width I, shared expert width Is (0: none), element type. */
+typedef struct {
+    int32_t hidden;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t inter;
+    int32_t shared_inter;
+    flint_dtype dtype;
+} flint_moe_dims;
+
+/* Device pointers to one layer's weights (layouts above).  The shared_* pointers
+ * are ignored when dims.shared_inter == 0. */
+typedef struct {
+    const void *router;
+    const float *router_bias;
+    const void *gate;
+    const void *up;
+    const void *down;
+    const void *shared_gate;
+    const void *shared_up;
+    const void *shared_down;
+} flint_moe_weights;
+
+/* Static, NUL-terminated description of a status code. */
+const char *flint_status_string(flint_status status);
+
+/* Bytes of device workspace that flint_moe_route, flint_moe_dispatch and
+ * flint_moe_forward need for T tokens of this shape (an upper bound valid for
+ * all three).  Returns 0 for an unsupported shape or T < 0.  The workspace is
+ * scratch: its contents on entry do not matter and are not preserved. */
+size_t flint_moe_workspace_bytes(const flint_moe_dims *dims, int32_t T);
+
+/* Router (serving-kit review, "The architecture, from the config": sigmoid
+ * scoring with normalised top-k).
+ *   x [T][H] (dims.dtype), router [E][H] (dims.dtype), router_bias [E] float32
+ *   or NULL (added to the logit before the sigmoid).
+ *   topk_idx [T][K] int32 out: the K selected experts, distinct, ascending.
+ *   topk_w   [T][K] float32 out: their weights s_e / sum of the selected s,
+ *            in the same order; each row sums to 1 up to float32 rounding.
+ *   ws / ws_bytes: device workspace of at least flint_moe_workspace_bytes. */
+flint_status flint_moe_route(const flint_moe_dims *dims, int32_t T, const void *x,
+                             const void *router, const float *router_bias,
+                             int32_t *topk_idx, float *topk_w,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch: the token -> expert assignment grouped by expert (release news page,
+ * "What runs on each token": a router picks 6 of 256 expert sub-networks for
+ * each token).
+ *   topk_idx [T][K] int32 in: each row K distinct experts in [0, E).  Rows need
+ *            not be sorted.  Out-of-range ids give undefined results.
+ *   expert_counts  [E]   out: tokens routed to each expert.
+ *   expert_offsets [E+1] out: exclusive prefix sum of the counts; [E] = T*K.
+ *   sorted_token [T*K] out: expert-major, token-ascending within an expert.
+ *   slot_of      [T*K] out: slot_of[t*K+k] is the position of the pair
+ *                (t, topk_idx[t][k]) in sorted_token.
+ *   The result is unique, so it is bit-exact and deterministic. */
+flint_status flint_moe_dispatch(const flint_moe_dims *dims, int32_t T, const int32_t *topk_idx,
+                                int32_t *expert_counts, int32_t *expert_offsets,
+                                int32_t *sorted_token, int32_t *slot_of,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer: router, dispatch, routed experts, shared expert, weighted
+ * combine (both pages cited above).
+ *   x [T][H] (dims.dtype); weights: device pointers, layouts above.
+ *   out [T][H]: out_dtype FLINT_F32 (float32) or FLINT_BF16 (rounded to
+ *               nearest even from the float32 sum).
+ *   topk_idx_out [T][K], topk_w_out [T][K]: optional (NULL to skip); the routing
+ *               used, as flint_moe_route defines it.
+ *   The result is deterministic: the same inputs give the same bits. */
+flint_status flint_moe_forward(const flint_moe_dims *dims, int32_t T, const void *x,
+                               const flint_moe_weights *weights, void *out,
+                               flint_dtype out_dtype, int32_t *topk_idx_out,
+                               float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
+
+/* flint_moe_forward with stage timing: identical arguments, results and
+ * kernels, plus `events`, an array of 6 hipEvent_t handles (created by the
+ * caller, passed as void*) that are recorded on `stream` before the router and
+ * after each stage: [0] start, [1] router logits, [2] top-k and dispatch,
+ * [3] gate/up + SwiGLU, [4] down projection, [5] combine.  The caller reads
+ * them with hipEventElapsedTime.  NULL `events` makes it flint_moe_forward. */
+flint_status flint_moe_forward_profiled(const flint_moe_dims *dims, int32_t T, const void *x,
+                                        const flint_moe_weights *weights, void *out,
+                                        flint_dtype out_dtype, int32_t *topk_idx_out,
+                                        float *topk_w_out, void *ws, size_t ws_bytes, void *stream,
+                                        void *const *events);
+
+/* RMSNorm between stacked MoE layers (unit gain): out = bf16(in / sqrt(mean(in^2) + eps)),
+ * the mean over each row of H values.  in [T][H] float32, out [T][H] bf16.
+ * H must be a multiple of 64 and at most 8192.  This joins consecutive layers in
+ * the stacked workload; the pages use RMSNorm on attention heads, not here. */
+flint_status flint_rmsnorm(int32_t T, int32_t H, const float *in, void *out_bf16, float eps,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLINT_MOE_H */

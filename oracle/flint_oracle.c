@@ -37,6 +37,9 @@
  * arithmetic is independent of the others and runs in the same order.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -156,23 +159,14 @@ int oracle_route(const oracle_dims *d, int T, const float *x, const float *wr,
 {
     if (!check_dims(d) || T < 0 || (T > 0 && (!x || !wr || !topk_idx || !topk_w)))
         return ORACLE_BAD_ARG;
-    const int H = d->hidden, E = d->n_experts, K = d->top_k;
-    int bad = 0;
-#pragma omp parallel
-    {
-        float *scores = (float *)malloc(sizeof(float) * (size_t)E);
-        if (!scores) {
-#pragma omp atomic write
-            bad = 1;
-        } else {
-#pragma omp for schedule(dynamic, 16)
-            for (int t = 0; t < T; ++t)
-                route_one(d, x + (size_t)t * H, wr, bias, scores, topk_idx + (size_t)t * K,
-                          topk_w + (size_t)t * K, near_tie ? near_tie + t : NULL);
-            free(scores);
-        }
+    const int H = d->hidden, K = d->top_k;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int t = 0; t < T; ++t) {
+        float scores[4096];
+        route_one(d, x + (size_t)t * H, wr, bias, scores, topk_idx + (size_t)t * K,
+                  topk_w + (size_t)t * K, near_tie ? near_tie + t : NULL);
     }
-    return bad ? ORACLE_BAD_ARG : ORACLE_OK;
+    return ORACLE_OK;
 }
 
 /* Sigmoid scores only (float32 values as defined above), [T][E]. */
@@ -290,51 +284,47 @@ int oracle_forward(const oracle_dims *d, int T, const float *x, const float *wr,
             if (force_idx[i] < 0 || force_idx[i] >= E) return ORACLE_BAD_ARG;
     int bad = 0;
     const int wmax = I > Is ? I : Is;
-#pragma omp parallel
-    {
-        float *scores = (float *)malloc(sizeof(float) * (size_t)E);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < T; ++t) {
+        float scores[4096];
+        int sel[64];
+        float w[64];
         double *hbuf = (double *)malloc(sizeof(double) * (size_t)wmax);
         double *y = (double *)malloc(sizeof(double) * (size_t)H);
         double *acc = (double *)malloc(sizeof(double) * (size_t)H);
-        int sel[64];
-        float w[64];
-        if (!scores || !hbuf || !y || !acc) {
+        if (!hbuf || !y || !acc) {
 #pragma omp atomic write
             bad = 1;
         } else {
-#pragma omp for schedule(dynamic, 1)
-            for (int t = 0; t < T; ++t) {
-                const float *xt = x + (size_t)t * H;
-                unsigned char tie = 0;
-                route_one(d, xt, wr, bias, scores, sel, w, &tie);
-                if (force_idx) {
-                    double sum = 0.0;
-                    for (int k = 0; k < K; ++k) {
-                        sel[k] = force_idx[(size_t)t * K + k];
-                        sum += (double)scores[sel[k]];
-                    }
-                    for (int k = 0; k < K; ++k) w[k] = (float)((double)scores[sel[k]] / sum);
-                }
-                for (int n = 0; n < H; ++n) acc[n] = 0.0;
+            const float *xt = x + (size_t)t * H;
+            unsigned char tie = 0;
+            route_one(d, xt, wr, bias, scores, sel, w, &tie);
+            if (force_idx) {
+                double sum = 0.0;
                 for (int k = 0; k < K; ++k) {
-                    const int e = sel[k];
-                    expert_one(d, I, xt, wg + (size_t)e * I * H, wu + (size_t)e * I * H,
-                               wd + (size_t)e * H * I, hbuf, y);
-                    for (int n = 0; n < H; ++n) acc[n] += (double)w[k] * y[n];
+                    sel[k] = force_idx[(size_t)t * K + k];
+                    sum += (double)scores[sel[k]];
                 }
-                if (Is > 0) {
-                    expert_one(d, Is, xt, wsg, wsu, wsd, hbuf, y);
-                    for (int n = 0; n < H; ++n) acc[n] += y[n];
-                }
-                for (int n = 0; n < H; ++n) out[(size_t)t * H + n] = (float)acc[n];
-                if (topk_idx_out)
-                    for (int k = 0; k < K; ++k) topk_idx_out[(size_t)t * K + k] = sel[k];
-                if (topk_w_out)
-                    for (int k = 0; k < K; ++k) topk_w_out[(size_t)t * K + k] = w[k];
-                if (near_tie) near_tie[t] = tie;
+                for (int k = 0; k < K; ++k) w[k] = (float)((double)scores[sel[k]] / sum);
             }
+            for (int n = 0; n < H; ++n) acc[n] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const int e = sel[k];
+                expert_one(d, I, xt, wg + (size_t)e * I * H, wu + (size_t)e * I * H,
+                           wd + (size_t)e * H * I, hbuf, y);
+                for (int n = 0; n < H; ++n) acc[n] += (double)w[k] * y[n];
+            }
+            if (Is > 0) {
+                expert_one(d, Is, xt, wsg, wsu, wsd, hbuf, y);
+                for (int n = 0; n < H; ++n) acc[n] += y[n];
+            }
+            for (int n = 0; n < H; ++n) out[(size_t)t * H + n] = (float)acc[n];
+            if (topk_idx_out)
+                for (int k = 0; k < K; ++k) topk_idx_out[(size_t)t * K + k] = sel[k];
+            if (topk_w_out)
+                for (int k = 0; k < K; ++k) topk_w_out[(size_t)t * K + k] = w[k];
+            if (near_tie) near_tie[t] = tie;
         }
-        free(scores);
         free(hbuf);
         free(y);
         free(acc);
@@ -383,4 +373,14 @@ void oracle_param_counts(const oracle_dims *d, int64_t *out)
     out[2] = 3 * H * I;
     out[3] = 3 * H * Is;
     out[4] = K * 3 * H * I + 3 * H * Is;
+}
+
+/* Threads the OpenMP loops over tokens use (1 without OpenMP). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -94,6 +94,8 @@ class Oracle:
             getattr(lib, f).restype = ctypes.c_int
         lib.oracle_round_bf16.restype = None
         lib.oracle_param_counts.restype = None
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -167,6 +169,10 @@ class Oracle:
         out = np.zeros_like(a)
         self.lib.oracle_round_bf16(_p(a), _p(out), a.size)
         return out
+
+    def threads(self) -> int:
+        """Threads the oracle's OpenMP loops use."""
+        return int(self.lib.oracle_threads())
 
     def param_counts(self, d: Dims):
         """(router, routed total, one expert, shared expert, active expert params per token)."""

@@ -1,0 +1,63 @@
+"""Loads libflint_moe.so (the HIP library) through ctypes.
+
+torch is imported first on purpose: the library's HIP runtime dependency
+(libamdhip64.so.7) then resolves to the copy torch already loaded, so streams
+and device pointers from torch are valid inside the library.  There is no
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (load order, see above)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libflint_moe.so")
+
+_lib = None
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("shared_gate", ctypes.c_void_p),
+                ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p)]
+
+
+EXPORTS = ("flint_status_string", "flint_moe_workspace_bytes", "flint_moe_route", "flint_moe_dispatch",
+           "flint_moe_forward", "flint_moe_forward_profiled", "flint_rmsnorm")
+
+
+def load():
+    """The loaded library (raises RuntimeError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(
+            f"{LIBRARY} is missing: build it with `python -m routed_expert_ffn_flint_amd.build` "
+            "(the Flint MoE layer has no CPU or PyTorch fallback)")
+    lib = ctypes.CDLL(LIBRARY)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(Dims)
+    lib.flint_status_string.argtypes = [I32]
+    lib.flint_status_string.restype = ctypes.c_char_p
+    lib.flint_moe_workspace_bytes.argtypes = [D, I32]
+    lib.flint_moe_workspace_bytes.restype = SZ
+    lib.flint_moe_route.argtypes = [D, I32, P, P, P, P, P, P, SZ, P]
+    lib.flint_moe_route.restype = I32
+    lib.flint_moe_dispatch.argtypes = [D, I32, P, P, P, P, P, P, SZ, P]
+    lib.flint_moe_dispatch.restype = I32
+    lib.flint_moe_forward.argtypes = [D, I32, P, ctypes.POINTER(Weights), P, I32, P, P, P, SZ, P]
+    lib.flint_moe_forward.restype = I32
+    lib.flint_moe_forward_profiled.argtypes = [D, I32, P, ctypes.POINTER(Weights), P, I32, P, P, P, SZ, P, P]
+    lib.flint_moe_forward_profiled.restype = I32
+    lib.flint_rmsnorm.argtypes = [I32, I32, P, P, ctypes.c_float, P]
+    lib.flint_rmsnorm.restype = I32
+    _lib = lib
+    return lib

@@ -1,0 +1,311 @@
+// C ABI of the Flint MoE layer: host-side validation, workspace carving and
+// launch sequencing.  Every check runs before the first launch, so an argument
+// error leaves the outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/flint_moe.h"
+#include "launch.hpp"
+
+using namespace flint;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by every entry point.  Returns FLINT_OK or an error.
+flint_status check_dims(const flint_moe_dims *d)
+{
+    if (!d) return FLINT_INVALID_ARG;
+    if (d->dtype != FLINT_F32 && d->dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
+    if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->inter <= 0 || d->shared_inter < 0)
+        return FLINT_INVALID_ARG;
+    if (d->top_k > d->n_experts) return FLINT_INVALID_ARG;
+    if (d->top_k > kMaxTopK || d->n_experts > kMaxExperts) return FLINT_UNSUPPORTED;
+    if (d->hidden % 64 || d->inter % 64 || d->shared_inter % 64) return FLINT_UNSUPPORTED;
+    if (d->hidden > 8192 || d->inter > 4096 || d->shared_inter > 4096) return FLINT_UNSUPPORTED;
+    return FLINT_OK;
+}
+
+flint_status check_T(const flint_moe_dims *d, int32_t T)
+{
+    if (T < 0) return FLINT_INVALID_ARG;
+    if ((int64_t)T * d->top_k >= (int64_t)1 << 31) return FLINT_UNSUPPORTED;
+    // slot indices times H must fit the kernels' size_t arithmetic; row counts fit int
+    if ((int64_t)T * d->top_k * d->hidden >= (int64_t)1 << 40) return FLINT_UNSUPPORTED;
+    return FLINT_OK;
+}
+
+int elem_bytes(const flint_moe_dims *d) { return d->dtype == FLINT_BF16 ? 2 : 4; }
+
+}  // namespace
+
+namespace flint {
+
+int list_capacity(int T, int K, int E, int bm)
+{
+    const long long pairs = (long long)T * K;
+    const long long nonempty = pairs < E ? pairs : E;
+    return (int)(pairs / bm + nonempty + 1);
+}
+
+Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int eb)
+{
+    Workspace w{};
+    const size_t TK = (size_t)T * K;
+    const int ntiles = (T + kTopkTile - 1) / kTopkTile;
+    const ExpertTiles tiles = expert_tiles_for(T);
+    const int cap1 = list_capacity(T, K, E, tiles.bm1);
+    const int cap2 = list_capacity(T, K, E, tiles.bm2);
+    size_t off = 0;
+    char *b = (char *)base;
+    auto take = [&](size_t bytes) -> void * {
+        void *p = b ? (void *)(b + off) : nullptr;
+        off += align_up(bytes ? bytes : 1);
+        return p;
+    };
+    w.logits = (float *)take((size_t)T * E * 4);
+    w.hist = (int32_t *)take((size_t)ntiles * E * 4);
+    w.tile_base = (int32_t *)take((size_t)ntiles * E * 4);
+    w.rank = (int32_t *)take(TK * 4);
+    w.topk_idx = (int32_t *)take(TK * 4);
+    w.topk_w = (float *)take(TK * 4);
+    w.counts = (int32_t *)take((size_t)E * 4);
+    w.offsets = (int32_t *)take((size_t)(E + 1) * 4);
+    w.sorted_token = (int32_t *)take(TK * 4);
+    w.slot_of = (int32_t *)take(TK * 4);
+    w.list1 = (int32_t *)take((size_t)cap1 * 8);
+    w.list2 = (int32_t *)take((size_t)cap2 * 8);
+    w.meta = (int32_t *)take(16);
+    w.h_sorted = take(TK * I * eb);
+    w.h_shared = take((size_t)T * Is * eb);
+    w.y_sorted = (float *)take(TK * H * 4);
+    w.y_shared = (float *)take((size_t)T * H * 4);
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace flint
+
+extern "C" {
+
+const char *flint_status_string(flint_status s)
+{
+    switch (s) {
+    case FLINT_OK: return "ok";
+    case FLINT_INVALID_ARG: return "invalid argument";
+    case FLINT_UNSUPPORTED: return "unsupported configuration (refused; there is no fallback path)";
+    case FLINT_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FLINT_DEVICE_ERROR: return "device error at launch";
+    default: return "unknown status";
+    }
+}
+
+size_t flint_moe_workspace_bytes(const flint_moe_dims *d, int32_t T)
+{
+    if (check_dims(d) != FLINT_OK || check_T(d, T) != FLINT_OK) return 0;
+    return plan_workspace(nullptr, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                          elem_bytes(d))
+        .bytes;
+}
+
+static flint_status check_ws(const flint_moe_dims *d, int32_t T, const void *ws, size_t ws_bytes)
+{
+    const size_t need = flint_moe_workspace_bytes(d, T);
+    if (ws_bytes < need) return FLINT_WORKSPACE_TOO_SMALL;
+    if (!ws) return FLINT_INVALID_ARG;
+    if (((uintptr_t)ws & (kAlign - 1)) != 0) return FLINT_UNSUPPORTED;
+    return FLINT_OK;
+}
+
+flint_status flint_moe_route(const flint_moe_dims *d, int32_t T, const void *x, const void *router,
+                             const float *router_bias, int32_t *topk_idx, float *topk_w, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    flint_status st = check_dims(d);
+    if (st != FLINT_OK) return st;
+    if ((st = check_T(d, T)) != FLINT_OK) return st;
+    if (T == 0) return FLINT_OK;
+    if (!x || !router || !topk_idx || !topk_w) return FLINT_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(router) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+        (router_bias && !aligned16(router_bias)))
+        return FLINT_UNSUPPORTED;
+    if ((st = check_ws(d, T, ws, ws_bytes)) != FLINT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                                 elem_bytes(d));
+    if (launch_router_logits(d->dtype == FLINT_BF16, x, T, d->hidden, router, router_bias, d->n_experts,
+                             w.logits, s) != hipSuccess)
+        return FLINT_DEVICE_ERROR;
+    DispatchArgs a{};
+    a.T = T;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    a.logits = w.logits;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.compute_topk = true;
+    a.dispatch = false;
+    if (launch_topk_dispatch(a, s) != hipSuccess) return FLINT_DEVICE_ERROR;
+    return FLINT_OK;
+}
+
+static DispatchArgs dispatch_args(const flint_moe_dims *d, int32_t T, const Workspace &w)
+{
+    DispatchArgs a{};
+    const ExpertTiles tiles = expert_tiles_for(T);
+    a.T = T;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    a.hist = w.hist;
+    a.tile_base = w.tile_base;
+    a.rank = w.rank;
+    a.list1 = w.list1;
+    a.list2 = w.list2;
+    a.meta = w.meta;
+    a.bm1 = tiles.bm1;
+    a.bm2 = tiles.bm2;
+    a.dispatch = true;
+    return a;
+}
+
+flint_status flint_moe_dispatch(const flint_moe_dims *d, int32_t T, const int32_t *topk_idx,
+                                int32_t *counts, int32_t *offsets, int32_t *sorted_token, int32_t *slot_of,
+                                void *ws, size_t ws_bytes, void *stream)
+{
+    flint_status st = check_dims(d);
+    if (st != FLINT_OK) return st;
+    if ((st = check_T(d, T)) != FLINT_OK) return st;
+    if (!counts || !offsets) return FLINT_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !sorted_token || !slot_of)) return FLINT_INVALID_ARG;
+    if (!aligned16(counts) || !aligned16(offsets) ||
+        (T > 0 && (!aligned16(topk_idx) || !aligned16(sorted_token) || !aligned16(slot_of))))
+        return FLINT_UNSUPPORTED;
+    if ((st = check_ws(d, T, ws, ws_bytes)) != FLINT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        // every count and offset is zero (a fill kernel, not a memset node, so
+        // that the call can be captured in a graph)
+        if (launch_fill_i32(counts, d->n_experts, 0, s) != hipSuccess) return FLINT_DEVICE_ERROR;
+        if (launch_fill_i32(offsets, d->n_experts + 1, 0, s) != hipSuccess) return FLINT_DEVICE_ERROR;
+        return FLINT_OK;
+    }
+    Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                                 elem_bytes(d));
+    DispatchArgs a = dispatch_args(d, T, w);
+    a.topk_idx = const_cast<int32_t *>(topk_idx);
+    a.compute_topk = false;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.sorted_token = sorted_token;
+    a.slot_of = slot_of;
+    if (launch_topk_dispatch(a, s) != hipSuccess) return FLINT_DEVICE_ERROR;
+    return FLINT_OK;
+}
+
+flint_status flint_moe_forward(const flint_moe_dims *d, int32_t T, const void *x, const flint_moe_weights *wt,
+                               void *out, flint_dtype out_dtype, int32_t *topk_idx_out, float *topk_w_out,
+                               void *ws, size_t ws_bytes, void *stream)
+{
+    return flint_moe_forward_profiled(d, T, x, wt, out, out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes, stream,
+                                      nullptr);
+}
+
+flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, const void *x,
+                                        const flint_moe_weights *wt, void *out, flint_dtype out_dtype,
+                                        int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                                        void *stream, void *const *events)
+{
+    flint_status st = check_dims(d);
+    if (st != FLINT_OK) return st;
+    if ((st = check_T(d, T)) != FLINT_OK) return st;
+    if (out_dtype != FLINT_F32 && out_dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
+    if (T == 0) return FLINT_OK;
+    if (!x || !wt || !out || !wt->router || !wt->gate || !wt->up || !wt->down) return FLINT_INVALID_ARG;
+    const bool has_shared = d->shared_inter > 0;
+    if (has_shared && (!wt->shared_gate || !wt->shared_up || !wt->shared_down)) return FLINT_INVALID_ARG;
+    const void *ptrs[] = {x, out, wt->router, wt->gate, wt->up, wt->down};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FLINT_UNSUPPORTED;
+    if (wt->router_bias && !aligned16(wt->router_bias)) return FLINT_UNSUPPORTED;
+    if (has_shared && (!aligned16(wt->shared_gate) || !aligned16(wt->shared_up) || !aligned16(wt->shared_down)))
+        return FLINT_UNSUPPORTED;
+    if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
+        return FLINT_UNSUPPORTED;
+    if ((st = check_ws(d, T, ws, ws_bytes)) != FLINT_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = d->dtype == FLINT_BF16;
+    Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                                 elem_bytes(d));
+    hipEvent_t const *ev = (hipEvent_t const *)events;
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return FLINT_DEVICE_ERROR;
+    if (launch_router_logits(bf16, x, T, d->hidden, wt->router, wt->router_bias, d->n_experts, w.logits, s) !=
+        hipSuccess)
+        return FLINT_DEVICE_ERROR;
+
+    DispatchArgs a = dispatch_args(d, T, w);
+    a.logits = w.logits;
+    a.topk_idx = topk_idx_out ? topk_idx_out : w.topk_idx;
+    a.topk_w = topk_w_out ? topk_w_out : w.topk_w;
+    a.compute_topk = true;
+    a.counts = w.counts;
+    a.offsets = w.offsets;
+    a.sorted_token = w.sorted_token;
+    a.slot_of = w.slot_of;
+    if (ev && hipEventRecord(ev[1], s) != hipSuccess) return FLINT_DEVICE_ERROR;
+    if (launch_topk_dispatch(a, s) != hipSuccess) return FLINT_DEVICE_ERROR;
+    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return FLINT_DEVICE_ERROR;
+
+    ExpertArgs e{};
+    e.bf16 = bf16;
+    e.T = T;
+    e.H = d->hidden;
+    e.E = d->n_experts;
+    e.K = d->top_k;
+    e.I = d->inter;
+    e.Is = d->shared_inter;
+    e.x = x;
+    e.gate = wt->gate;
+    e.up = wt->up;
+    e.down = wt->down;
+    e.shared_gate = wt->shared_gate;
+    e.shared_up = wt->shared_up;
+    e.shared_down = wt->shared_down;
+    e.sorted_token = w.sorted_token;
+    e.offsets = w.offsets;
+    e.slot_of = w.slot_of;
+    e.topk_w = a.topk_w;
+    e.list1 = w.list1;
+    e.list2 = w.list2;
+    e.meta = w.meta;
+    e.h_sorted = w.h_sorted;
+    e.h_shared = w.h_shared;
+    e.y_sorted = w.y_sorted;
+    e.y_shared = w.y_shared;
+    e.out = out;
+    e.out_bf16 = out_dtype == FLINT_BF16;
+    e.tiles = expert_tiles_for(T);
+    if (launch_experts(e, s, ev ? ev + 3 : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
+    return FLINT_OK;
+}
+
+flint_status flint_rmsnorm(int32_t T, int32_t H, const float *in, void *out_bf16, float eps, void *stream)
+{
+    if (T < 0 || H <= 0) return FLINT_INVALID_ARG;
+    if (H % 64 || H > 8192) return FLINT_UNSUPPORTED;
+    if (T == 0) return FLINT_OK;
+    if (!in || !out_bf16) return FLINT_INVALID_ARG;
+    if (!aligned16(in) || !aligned16(out_bf16)) return FLINT_UNSUPPORTED;
+    if (!(eps >= 0.0f)) return FLINT_INVALID_ARG;
+    if (launch_rmsnorm(T, H, in, (uint16_t *)out_bf16, eps, (hipStream_t)stream) != hipSuccess)
+        return FLINT_DEVICE_ERROR;
+    return FLINT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,338 @@
+// Expert kernels of the Flint MoE layer (gfx950): grouped gate/up GEMM with a
+// fused SwiGLU, grouped down GEMM, weighted combine.
+//
+// Layer (serving-kit review, "The architecture, from the config"; release news
+// page, "What runs on each token"): each token runs its K selected experts of
+// width I and an always-on shared expert of width Is; the gated three-matrix
+// expert form fits the serving-kit review's parameter count.
+//
+//   k_gate_up  h[slot][c] = silu(gate[e][c] . x[tok]) * (up[e][c] . x[tok])  -> dtype
+//              routed rows are gathered through sorted_token; the shared expert
+//              is the same kernel over all T tokens with its own weights.
+//   k_down     y[slot][n] = down[e][n] . h[slot]                             -> float32
+//   k_combine  out[t] = sum_k w[t][k] * y[slot_of[t][k]] + y_shared[t]        -> out dtype
+//
+// Work items: the shared expert's tiles come first (their number is known on
+// the host), then the routed tiles listed on the device by the dispatch
+// kernel.  The grid covers the list's capacity; items past the list's actual
+// length exit at once, so the host never reads a device count.
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace flint {
+
+template <bool SPLITK> struct WaveGrid;
+template <> struct WaveGrid<true> {   // 4 waves, same tile, k split in four
+    static constexpr int WM = 1, WN = 1;
+};
+template <> struct WaveGrid<false> {  // 4 waves in a 2x2 grid, all of k each
+    static constexpr int WM = 2, WN = 2;
+};
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU.  A wave's NB column blocks are NB/2 gate blocks and the NB/2
+// up blocks of the same channels, so silu(g)*u pairs up in registers.
+template <typename DT, int MB, int NB, bool SPLITK>
+__global__ __launch_bounds__(256) void k_gate_up(ExpertArgs a, int n_shared_items)
+{
+    using S = typename DT::storage;
+    constexpr int WM = WaveGrid<SPLITK>::WM, WN = WaveGrid<SPLITK>::WN;
+    constexpr int BM = WM * MB * 16, HALF = NB / 2, BN = WN * HALF * 16;
+    __shared__ float red[SPLITK ? 4 * MB * NB * 256 : 1];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = SPLITK ? 0 : wave / WN, wn = SPLITK ? 0 : wave % WN;
+    const int H = a.H;
+    const S *x = (const S *)a.x;
+
+    int item = blockIdx.x;
+    const bool shared = item < n_shared_items;
+    int width, row0, row_end, n0;
+    const S *wg, *wu;
+    S *hout;
+    const int32_t *gather = nullptr;
+    if (shared) {
+        const int ntn = a.Is / BN;
+        row0 = (item / ntn) * BM;
+        n0 = (item % ntn) * BN;
+        row_end = a.T;
+        width = a.Is;
+        wg = (const S *)a.shared_gate;
+        wu = (const S *)a.shared_up;
+        hout = (S *)a.h_shared;
+    } else {
+        item -= n_shared_items;
+        const int ntn = a.I / BN;
+        const int entry = item / ntn;
+        if (entry >= a.meta[0]) return;
+        const int e = a.list1[2 * entry];
+        row0 = a.list1[2 * entry + 1];
+        row_end = a.offsets[e + 1];
+        n0 = (item % ntn) * BN;
+        width = a.I;
+        wg = (const S *)a.gate + (size_t)e * a.I * H;
+        wu = (const S *)a.up + (size_t)e * a.I * H;
+        hout = (S *)a.h_sorted;
+        gather = a.sorted_token;
+    }
+
+    const int kg = (lane >> 4) * 8;
+    const int rbase = row0 + wm * MB * 16;
+    const S *a_rows[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        int r = rbase + m * 16 + (lane & 15);
+        if (r >= row_end) r = row0;
+        const int tok = gather ? gather[r] : r;
+        a_rows[m] = x + (size_t)tok * H + kg;
+    }
+    const int cbase = n0 + wn * HALF * 16;
+    const S *b_rows[NB];
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+        const int c = cbase + j * 16 + (lane & 15);
+        b_rows[j] = wg + (size_t)c * H + kg;
+        b_rows[j + HALF] = wu + (size_t)c * H + kg;
+    }
+
+    f32x4 acc[MB][NB];
+    zero_acc(acc);
+    const int nslices = H / 32;
+    int s0 = 0, s1 = nslices;
+    if (SPLITK) {
+        const int per = (nslices + 3) / 4;
+        s0 = min(wave * per, nslices);
+        s1 = min(s0 + per, nslices);
+    }
+    wave_gemm<DT, MB, NB, 4>(a_rows, b_rows, s0, s1, acc);
+    if (SPLITK) splitk_reduce4(acc, red);
+
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+        if (SPLITK && (j % 4) != wave) continue;  // spread the stores over the waves
+        const int c = cbase + j * 16 + (lane & 15);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rbase + m * 16 + (lane >> 4) * 4 + i;
+                if (r < row_end)
+                    store_elem<DT>(hout + (size_t)r * width + c, swiglu(acc[m][j][i], acc[m][j + HALF][i]));
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Down projection: y[row][n] = down[n] . h[row], float32 out.
+template <typename DT, int MB, int NB, bool SPLITK>
+__global__ __launch_bounds__(256) void k_down(ExpertArgs a, int n_shared_items)
+{
+    using S = typename DT::storage;
+    constexpr int WM = WaveGrid<SPLITK>::WM, WN = WaveGrid<SPLITK>::WN;
+    constexpr int BM = WM * MB * 16, BN = WN * NB * 16;
+    __shared__ float red[SPLITK ? 4 * MB * NB * 256 : 1];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = SPLITK ? 0 : wave / WN, wn = SPLITK ? 0 : wave % WN;
+    const int H = a.H;
+    const int ntn = (H + BN - 1) / BN;
+
+    int item = blockIdx.x;
+    const bool shared = item < n_shared_items;
+    int kdim, row0, row_end, n0;
+    const S *hin, *wd;
+    float *yout;
+    if (shared) {
+        row0 = (item / ntn) * BM;
+        n0 = (item % ntn) * BN;
+        row_end = a.T;
+        kdim = a.Is;
+        hin = (const S *)a.h_shared;
+        wd = (const S *)a.shared_down;
+        yout = a.y_shared;
+    } else {
+        item -= n_shared_items;
+        const int entry = item / ntn;
+        if (entry >= a.meta[1]) return;
+        const int e = a.list2[2 * entry];
+        row0 = a.list2[2 * entry + 1];
+        row_end = a.offsets[e + 1];
+        n0 = (item % ntn) * BN;
+        kdim = a.I;
+        hin = (const S *)a.h_sorted;
+        wd = (const S *)a.down + (size_t)e * H * a.I;
+        yout = a.y_sorted;
+    }
+
+    const int kg = (lane >> 4) * 8;
+    const int rbase = row0 + wm * MB * 16;
+    const S *a_rows[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        int r = rbase + m * 16 + (lane & 15);
+        if (r >= row_end) r = row0;
+        a_rows[m] = hin + (size_t)r * kdim + kg;
+    }
+    const int cbase = n0 + wn * NB * 16;
+    const S *b_rows[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+        int c = cbase + n * 16 + (lane & 15);
+        if (c >= H) c = 0;
+        b_rows[n] = wd + (size_t)c * kdim + kg;
+    }
+
+    f32x4 acc[MB][NB];
+    zero_acc(acc);
+    const int nslices = kdim / 32;
+    int s0 = 0, s1 = nslices;
+    if (SPLITK) {
+        const int per = (nslices + 3) / 4;
+        s0 = min(wave * per, nslices);
+        s1 = min(s0 + per, nslices);
+    }
+    wave_gemm<DT, MB, NB, 4>(a_rows, b_rows, s0, s1, acc);
+    if (SPLITK) splitk_reduce4(acc, red);
+
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+        if (SPLITK && (n % 4) != wave) continue;
+        const int c = cbase + n * 16 + (lane & 15);
+        if (c >= H) continue;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rbase + m * 16 + (lane >> 4) * 4 + i;
+                if (r < row_end) yout[(size_t)r * H + c] = acc[m][n][i];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// out[t] = sum_k w[t][k] * y_sorted[slot_of[t*K+k]] + y_shared[t]   (fixed order)
+__global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
+{
+    const int t = blockIdx.x;
+    const int H = a.H, K = a.K;
+    int slots[kMaxTopK];
+    float w[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        slots[k] = k < K ? a.slot_of[(size_t)t * K + k] : 0;
+        w[k] = k < K ? a.topk_w[(size_t)t * K + k] : 0.f;
+    }
+    for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            if (k < K) {
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
+                acc[0] += w[k] * y[0];
+                acc[1] += w[k] * y[1];
+                acc[2] += w[k] * y[2];
+                acc[3] += w[k] * y[3];
+            }
+        }
+        if (a.Is > 0) {
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c);
+            acc[0] += y[0];
+            acc[1] += y[1];
+            acc[2] += y[2];
+            acc[3] += y[3];
+        }
+        if (a.out_bf16) {
+            uint16_t *o = (uint16_t *)a.out + (size_t)t * H + c;
+            o[0] = f32_to_bf16(acc[0]);
+            o[1] = f32_to_bf16(acc[1]);
+            o[2] = f32_to_bf16(acc[2]);
+            o[3] = f32_to_bf16(acc[3]);
+        } else {
+            *reinterpret_cast<f32x4 *>((float *)a.out + (size_t)t * H + c) = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+ExpertTiles expert_tiles_for(int T)
+{
+    // Small batches (decode): split-k kernels over 32-row tiles, so that one
+    // tile holds every row an expert gets and each weight is read once.
+    if (T <= 512) return ExpertTiles{32, 32, 32, 64, true};
+    return ExpertTiles{128, 64, 128, 128, false};
+}
+
+template <typename DT>
+static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev)
+{
+    const ExpertTiles &t = a.tiles;
+    const int cap1 = list_capacity(a.T, a.K, a.E, t.bm1);
+    const int cap2 = list_capacity(a.T, a.K, a.E, t.bm2);
+    const int mt1 = (a.T + t.bm1 - 1) / t.bm1, mt2 = (a.T + t.bm2 - 1) / t.bm2;
+    const int ns1 = a.Is > 0 ? mt1 * (a.Is / t.bn1) : 0;
+    const int ns2 = a.Is > 0 ? mt2 * ((a.H + t.bn2 - 1) / t.bn2) : 0;
+    const int g1 = ns1 + cap1 * (a.I / t.bn1);
+    const int g2 = ns2 + cap2 * ((a.H + t.bn2 - 1) / t.bn2);
+    if (t.small)
+        k_gate_up<DT, 2, 4, true><<<g1, 256, 0, stream>>>(a, ns1);
+    else
+        k_gate_up<DT, 4, 4, false><<<g1, 256, 0, stream>>>(a, ns1);
+    if (ev) (void)hipEventRecord(ev[0], stream);
+    if (t.small)
+        k_down<DT, 2, 4, true><<<g2, 256, 0, stream>>>(a, ns2);
+    else
+        k_down<DT, 4, 4, false><<<g2, 256, 0, stream>>>(a, ns2);
+    if (ev) (void)hipEventRecord(ev[1], stream);
+    k_combine<<<a.T, 256, 0, stream>>>(a);
+    if (ev) (void)hipEventRecord(ev[2], stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev)
+{
+    if (a.T <= 0) return hipSuccess;
+    return a.bf16 ? launch_experts_t<BF16>(a, stream, ev) : launch_experts_t<F32>(a, stream, ev);
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm between stacked layers: out = bf16(in / sqrt(mean(in^2) + eps)).
+// Sum of squares and the scaling in double; the double result is rounded to
+// float with round-to-odd and then to bf16 with round-to-nearest-even, which
+// together round the double once to nearest-even bf16.
+__device__ __forceinline__ uint16_t f64_to_bf16(double d)
+{
+    float f = (float)d;
+    if ((double)f != d) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(d)) u -= 1u;  // step back toward zero
+        u |= 1u;
+        f = __uint_as_float(u);
+    }
+    return f32_to_bf16(f);
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ in, int H, float eps,
+                                                 uint16_t *__restrict__ out)
+{
+    __shared__ double part[4];
+    const int t = blockIdx.x;
+    const float *row = in + (size_t)t * H;
+    double ss = 0.0;
+    for (int c = threadIdx.x; c < H; c += blockDim.x) ss += (double)row[c] * (double)row[c];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const double tot = part[0] + part[1] + part[2] + part[3];
+    const double r = 1.0 / sqrt(tot / (double)H + (double)eps);
+    for (int c = threadIdx.x; c < H; c += blockDim.x) out[(size_t)t * H + c] = f64_to_bf16((double)row[c] * r);
+}
+
+hipError_t launch_rmsnorm(int T, int H, const float *in, uint16_t *out, float eps, hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+    k_rmsnorm<<<T, 256, 0, stream>>>(in, H, eps, out);
+    return hipGetLastError();
+}
+
+}  // namespace flint

@@ -1,0 +1,97 @@
+// Host-side launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace flint {
+
+// Tokens per work-group in the top-k / dispatch kernels.
+constexpr int kTopkTile = 256;
+// Maximum supported sizes.
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+
+// Tile shapes of the expert kernels for one launch regime.
+struct ExpertTiles {
+    int bm1;  // rows per gate/up tile
+    int bn1;  // intermediate channels per gate/up tile
+    int bm2;  // rows per down tile
+    int bn2;  // output columns per down tile
+    bool small;  // split-k decode kernels (true) or tiled kernels (false)
+};
+
+ExpertTiles expert_tiles_for(int T);
+
+// Device pointers carved out of the caller's workspace.
+struct Workspace {
+    float *logits;        // [T][E]
+    int32_t *hist;        // [ntiles][E]
+    int32_t *tile_base;   // [ntiles][E]
+    int32_t *rank;        // [T*K]
+    int32_t *topk_idx;    // [T*K] (used when the caller passes none)
+    float *topk_w;        // [T*K]
+    int32_t *counts;      // [E]
+    int32_t *offsets;     // [E+1]
+    int32_t *sorted_token;  // [T*K]
+    int32_t *slot_of;     // [T*K]
+    int32_t *list1;       // [2*cap1] gate/up tile list (expert, first slot)
+    int32_t *list2;       // [2*cap2] down tile list
+    int32_t *meta;        // [4]: list1 length, list2 length
+    void *h_sorted;       // [T*K][I] dtype
+    void *h_shared;       // [T][Is] dtype
+    float *y_sorted;      // [T*K][H]
+    float *y_shared;      // [T][H]
+    size_t bytes;         // total bytes needed
+};
+
+// Computes the layout for (T, dims); with base == nullptr only .bytes is valid.
+Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int elem_bytes);
+
+int list_capacity(int T, int K, int E, int bm);
+
+// ---- launches (all enqueue on `stream`, return hipGetLastError()) ----------
+
+// logits[t][e] = x[t] . router[e] (+ bias[e]), float32.
+hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const void *router,
+                                const float *bias, int E, float *logits, hipStream_t stream);
+
+// Top-k selection and/or dispatch.  See route.hip for the modes.
+struct DispatchArgs {
+    int T, E, K;
+    const float *logits;      // when compute_topk
+    int32_t *topk_idx;        // out when compute_topk, in otherwise
+    float *topk_w;            // out when compute_topk
+    bool compute_topk;
+    bool dispatch;            // also produce counts/offsets/sorted_token/slot_of (+ tile lists)
+    int32_t *hist, *tile_base, *rank;
+    int32_t *counts, *offsets, *sorted_token, *slot_of;
+    int32_t *list1, *list2, *meta;
+    int bm1, bm2;
+};
+hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream);
+
+struct ExpertArgs {
+    bool bf16;
+    int T, H, E, K, I, Is;
+    const void *x;
+    const void *gate, *up, *down;
+    const void *shared_gate, *shared_up, *shared_down;
+    const int32_t *sorted_token, *offsets, *slot_of;
+    const float *topk_w;
+    const int32_t *list1, *list2, *meta;
+    void *h_sorted, *h_shared;
+    float *y_sorted, *y_shared;
+    void *out;
+    bool out_bf16;
+    ExpertTiles tiles;
+};
+// stage_events (nullable): 3 events recorded after gate/up, down and combine.
+hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
+
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream);
+
+hipError_t launch_rmsnorm(int T, int H, const float *in, uint16_t *out, float eps, hipStream_t stream);
+
+}  // namespace flint

@@ -1,0 +1,147 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+sizes its workspace, and refuses bad arguments on the host before any launch.
+
+Only paths that return before the first kernel launch are exercised here; the
+pointers passed are never dereferenced (validation looks at them as integers).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from routed_expert_ffn_flint_amd import _lib, api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flint_moe.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+FAKE_WS = 0x100000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIBRARY):
+        from routed_expert_ffn_flint_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(flint_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and nothing C++-mangled is needed to use it: the exported names are plain
+    out = os.popen(f"nm -D --defined-only {_lib.LIBRARY}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def flint_dims(**kw):
+    base = dict(hidden=2048, n_experts=256, top_k=6, inter=512, shared_inter=1024, dtype=api.BF16)
+    base.update(kw)
+    return api.make_dims(**base)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert api.flint_status_string(code)
+    assert "unknown" in api.flint_status_string(99)
+
+
+def test_workspace_bytes(lib):
+    d = flint_dims()
+    small = api.flint_moe_workspace_bytes(d, 32)
+    big = api.flint_moe_workspace_bytes(d, 16384)
+    assert 0 < small < big
+    # holds at least the float32 expert outputs of every (token, expert) pair
+    assert big >= 16384 * 6 * 2048 * 4
+    assert api.flint_moe_workspace_bytes(d, 0) > 0
+    assert api.flint_moe_workspace_bytes(d, -1) == 0
+    assert api.flint_moe_workspace_bytes(flint_dims(top_k=9), 32) == 0
+    assert api.flint_moe_workspace_bytes(flint_dims(hidden=2000), 32) == 0
+
+
+def _forward(lib, d, T, ws_bytes=None, x=FAKE, out=FAKE, out_dtype=api.F32, w=None, ws=FAKE_WS):
+    if w is None:
+        w = _lib.Weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    if ws_bytes is None:
+        ws_bytes = api.flint_moe_workspace_bytes(d, T) if T >= 0 else 0
+    return lib.flint_moe_forward(ctypes.byref(d), T, x, ctypes.byref(w), out, out_dtype, None, None, ws,
+                                 ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=9), api.UNSUPPORTED),
+    (dict(n_experts=257, top_k=6), api.UNSUPPORTED),
+    (dict(top_k=0), api.INVALID_ARG),
+    (dict(n_experts=4, top_k=6), api.INVALID_ARG),
+    (dict(hidden=2000), api.UNSUPPORTED),
+    (dict(inter=500), api.UNSUPPORTED),
+    (dict(shared_inter=1000), api.UNSUPPORTED),
+    (dict(shared_inter=-64), api.INVALID_ARG),
+    (dict(dtype=7), api.UNSUPPORTED),
+    (dict(hidden=16384), api.UNSUPPORTED),
+])
+def test_forward_refuses_unsupported_shapes(lib, kw, status):
+    d = flint_dims(**kw)
+    assert _forward(lib, d, 32, ws_bytes=1 << 30) == status
+
+
+def test_forward_argument_errors(lib):
+    d = flint_dims()
+    assert _forward(lib, d, -1) == api.INVALID_ARG
+    assert _forward(lib, d, 0) == api.OK  # no-op, nothing launched
+    assert _forward(lib, d, 32, x=None) == api.INVALID_ARG
+    assert _forward(lib, d, 32, out=None) == api.INVALID_ARG
+    assert _forward(lib, d, 32, x=FAKE + 2) == api.UNSUPPORTED  # misaligned
+    assert _forward(lib, d, 32, out_dtype=5) == api.UNSUPPORTED
+    need = api.flint_moe_workspace_bytes(d, 32)
+    assert _forward(lib, d, 32, ws_bytes=need - 1) == api.WORKSPACE_TOO_SMALL
+    assert _forward(lib, d, 32, ws=None) == api.INVALID_ARG
+    assert _forward(lib, d, 32, ws=FAKE_WS + 16) == api.UNSUPPORTED  # workspace must be 256-byte aligned
+    no_shared = _lib.Weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
+    assert _forward(lib, d, 32, w=no_shared) == api.INVALID_ARG
+    no_gate = _lib.Weights(FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert _forward(lib, d, 32, w=no_gate) == api.INVALID_ARG
+    assert _forward(lib, d, 1 << 30) == api.UNSUPPORTED  # T*K overflows int32
+
+
+def test_route_and_dispatch_argument_errors(lib):
+    d = flint_dims()
+    need = api.flint_moe_workspace_bytes(d, 32)
+    r = lib.flint_moe_route
+    assert r(ctypes.byref(d), -1, FAKE, FAKE, None, FAKE, FAKE, FAKE_WS, need, None) == api.INVALID_ARG
+    assert r(ctypes.byref(d), 0, None, None, None, None, None, None, 0, None) == api.OK
+    assert r(ctypes.byref(d), 32, None, FAKE, None, FAKE, FAKE, FAKE_WS, need, None) == api.INVALID_ARG
+    assert r(ctypes.byref(d), 32, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE_WS, need, None) == api.UNSUPPORTED
+    assert r(ctypes.byref(d), 32, FAKE, FAKE, None, FAKE, FAKE, FAKE_WS, need - 1, None) == api.WORKSPACE_TOO_SMALL
+    dd = lib.flint_moe_dispatch
+    assert dd(ctypes.byref(d), 32, FAKE, None, FAKE, FAKE, FAKE, FAKE_WS, need, None) == api.INVALID_ARG
+    assert dd(ctypes.byref(d), 32, None, FAKE, FAKE, FAKE, FAKE, FAKE_WS, need, None) == api.INVALID_ARG
+    assert dd(ctypes.byref(d), -3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, need, None) == api.INVALID_ARG
+    bad = flint_dims(top_k=9)
+    assert dd(ctypes.byref(bad), 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, need, None) == api.UNSUPPORTED
+
+
+def test_rmsnorm_argument_errors(lib):
+    f = lib.flint_rmsnorm
+    assert f(-1, 2048, FAKE, FAKE, 1e-6, None) == api.INVALID_ARG
+    assert f(4, 100, FAKE, FAKE, 1e-6, None) == api.UNSUPPORTED
+    assert f(0, 2048, None, None, 1e-6, None) == api.OK
+    assert f(4, 2048, None, FAKE, 1e-6, None) == api.INVALID_ARG
+    assert f(4, 2048, FAKE, FAKE, -1.0, None) == api.INVALID_ARG
+
+
+def test_binding_raises_on_refusal(lib):
+    with pytest.raises(api.FlintError) as ei:
+        api.workspace(flint_dims(top_k=9), 32, device="cpu")
+    assert ei.value.status == api.UNSUPPORTED

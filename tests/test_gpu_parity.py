@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path, called through the C ABI, against the oracle.
+
+Small cases run the oracle on every token, with shapes chosen to span several
+tiles and leave ragged tails (T not a multiple of the 16/32/128-row tiles or the
+256-token dispatch tile; expert counts that are not multiples of 16).  The
+named workloads run at full size: routing of every token is checked, the
+dispatch permutation is checked bit for bit, and the outputs of sampled tokens
+are recomputed by the oracle one by one.  Bars are in gpu_common.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_common as G
+import oracle_pins
+from oracle import oracle as orc
+from routed_expert_ffn_flint_amd import api, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    G.require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _layer(wl, device="cuda"):
+    # small layers are drawn on the CPU generator and copied, large ones drawn on the GPU
+    if wl.n_experts * wl.inter * wl.hidden <= (1 << 24):
+        w = inputs.make_layer(wl, 0, "cpu")
+        w = {k: (v.to(device) if v is not None else None) for k, v in w.items()}
+        x = inputs.make_tokens(wl, device="cpu").to(device)
+    else:
+        w = inputs.make_layer(wl, 0, device)
+        x = inputs.make_tokens(wl, device=device)
+    return w, x
+
+
+SMALL = [
+    # name,       T,  H,   E,  K, I,   Is,  bf16,  bias
+    ("t1",        1,  128, 16, 2, 64,  64,  True,  False),
+    ("t5_noshr",  5,  64,  8,  3, 64,  0,   True,  False),
+    ("t17_e20",   17, 192, 20, 3, 128, 64,  True,  True),
+    ("t33",       33, 256, 32, 6, 64,  128, True,  False),
+    ("t40_kE",    40, 128, 8,  8, 64,  64,  True,  False),
+    ("t64_k1",    64, 128, 16, 1, 128, 64,  True,  True),
+    ("t100_f32",  100, 128, 24, 4, 64, 128, False, True),
+    ("t300",      300, 256, 64, 6, 128, 128, True, False),   # two dispatch tiles
+    ("t600_f32",  600, 128, 16, 2, 64, 64,  False, False),
+    ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_forward_small_every_token(case):
+    name, T, H, E, K, I, Is, bf16, bias = case
+    wl = inputs.custom(name, T, H, E, K, I, Is, bf16, seed=3, zipf=bias)
+    w, x = _layer(wl)
+    st = G.parity_full(wl, w, x)
+    print(f"{name}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
+
+
+def test_forward_bf16_output():
+    wl = inputs.custom("bf16out", 48, 256, 16, 4, 64, 64, True, seed=4)
+    w, x = _layer(wl)
+    G.parity_full(wl, w, x, out_dtype=torch.bfloat16)
+
+
+def test_toy_workload():
+    wl = inputs.WORKLOADS["toy"]
+    w, x = _layer(wl)
+    st = G.parity_full(wl, w, x)
+    assert st["rel_err"] < 1e-4  # fp32 throughout: far inside the bar
+    print(f"toy: rel_err={st['rel_err']:.3g}")
+
+
+def test_decode32_every_token():
+    wl = inputs.WORKLOADS["decode32"]
+    w, x = _layer(wl)
+    st = G.parity_full(wl, w, x)
+    print(f"decode32: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']} "
+          f"distinct experts={len(np.unique(st['idx']))}")
+
+
+def _check_dispatch_of(wl, gi):
+    d = api.dims_of(wl)
+    idx_dev = torch.from_numpy(gi).to("cuda")
+    counts, offsets, st_, so = [t.cpu().numpy() for t in api.dispatch(d, idx_dev)]
+    torch.cuda.synchronize()
+    oc, oo, ost, oso = orc.dispatch(G.oracle_dims(wl), gi)
+    np.testing.assert_array_equal(counts, oc)
+    np.testing.assert_array_equal(offsets, oo)
+    np.testing.assert_array_equal(st_, ost)
+    np.testing.assert_array_equal(so, oso)
+    return counts
+
+
+@pytest.mark.parametrize("name", ["prefill4096", "skew16384"])
+def test_full_size_layer_sampled(name):
+    wl = inputs.WORKLOADS[name]
+    w, x = _layer(wl)
+    T = wl.T
+    rng = np.random.default_rng(1)
+    sample = list(rng.choice(T, 48, replace=False)) + [0, T - 1]
+    # include tokens of the most loaded expert (several row tiles of it)
+    st = G.parity_sampled(wl, w, x, sample)
+    counts = _check_dispatch_of(wl, st["idx"])
+    hot = int(np.argmax(counts))
+    hot_tokens = np.nonzero((st["idx"] == hot).any(1))[0]
+    extra = list(hot_tokens[:: max(1, len(hot_tokens) // 16)][:16])
+    G.parity_sampled(wl, w, x, extra)
+    mean = counts.mean()
+    print(f"{name}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']} max/mean load "
+          f"{counts.max() / mean:.1f} min {counts.min()} experts>10x mean {(counts > 10 * mean).sum()}")
+    if wl.zipf_bias:
+        assert counts.max() > 10 * mean  # the skewed workload really is skewed
+
+
+def test_stack47_layer_by_layer():
+    """47 distinct layers resident in HBM, RMSNorm between layers.  Each layer is
+    checked against the oracle fed the GPU's own input to that layer (a flipped
+    near tie would otherwise cascade), on sampled tokens; each RMSNorm is checked
+    on every token."""
+    wl = inputs.WORKLOADS["stack47"]
+    d = api.dims_of(wl)
+    layers = [inputs.make_layer(wl, l, "cuda") for l in range(wl.layers)]
+    x = inputs.make_tokens(wl, device="cuda")
+    ws = api.workspace(d, wl.T)
+    rng = np.random.default_rng(7)
+    eps = float(np.float32(1e-6))
+    worst = 0.0
+    ties = 0
+    for l, w in enumerate(layers):
+        sample = rng.choice(wl.T, 6, replace=False)
+        one = inputs.Workload(f"stack47/L{l}", wl.T, wl.hidden, wl.n_experts, wl.top_k, wl.inter,
+                              wl.shared_inter, True, wl.seed)
+        st = G.parity_sampled(one, w, x, sample)
+        worst = max(worst, st["rel_err"])
+        ties += st["near_ties"]
+        if l % 8 == 0:
+            print(f"stack47 layer {l}: rel_err={st['rel_err']:.3g}", flush=True)
+        if l + 1 < wl.layers:
+            y = st["out"]
+            x = api.rmsnorm(y, eps)
+            torch.cuda.synchronize()
+            ref = orc.rmsnorm(y.cpu().numpy(), eps)
+            np.testing.assert_array_equal(x.float().cpu().numpy(), ref)
+    del ws
+    print(f"stack47: worst rel_err={worst:.3g} near_ties={ties}")
+
+
+@pytest.mark.parametrize("case", [(1, 16, 2), (100, 16, 6), (256, 256, 6), (257, 64, 8), (1000, 256, 6),
+                                  (5000, 256, 1), (3000, 20, 3)])
+def test_dispatch_random_assignments(case):
+    T, E, K = case
+    rng = np.random.default_rng(T + E + K)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)  # rows unsorted
+    wl = inputs.custom("disp", T, 64, E, K, 64, 0, True)
+    counts = _check_dispatch_of(wl, idx)
+    oracle_pins.check_dispatch_invariants(idx, E, counts, *[t for t in orc.dispatch(G.oracle_dims(wl), idx)[1:]])
+
+
+def test_route_entry_point_matches_forward_routing():
+    wl = inputs.WORKLOADS["decode32"]
+    w, x = _layer(wl)
+    d = api.dims_of(wl)
+    idx, tw = api.route(d, x, w["router"], w.get("bias"))
+    _, idx2, tw2 = G.gpu_layer(wl, w, x)
+    assert torch.equal(idx, idx2) and torch.equal(tw, tw2)
+
+
+@pytest.mark.parametrize("name", ["decode32", "prefill4096"])
+def test_deterministic(name):
+    wl = inputs.WORKLOADS[name]
+    w, x = _layer(wl)
+    a, ia, wa = G.gpu_layer(wl, w, x)
+    b, ib, wb = G.gpu_layer(wl, w, x)
+    assert torch.equal(ia, ib) and torch.equal(wa, wb)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_empty_batch_is_a_noop():
+    wl = inputs.WORKLOADS["decode32"]
+    d = api.dims_of(wl)
+    w, _ = _layer(wl)
+    x = torch.empty((0, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    out = api.forward(d, x, w)
+    torch.cuda.synchronize()
+    assert out.shape == (0, wl.hidden)
+    counts, offsets, _, _ = api.dispatch(d, torch.empty((0, wl.top_k), dtype=torch.int32, device="cuda"))
+    assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
+
+
+def test_rmsnorm_matches_oracle():
+    y = torch.randn((300, 2048), generator=torch.Generator().manual_seed(5)) * 3
+    eps = float(np.float32(1e-6))
+    got = api.rmsnorm(y.to("cuda"), eps).float().cpu().numpy()
+    np.testing.assert_array_equal(got, orc.rmsnorm(y.numpy(), eps))
