@@ -44,7 +44,21 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true", help="replay the steps from a captured HIP graph")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 5 times (reference for the HBM "
+                        "byte counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n}, "launches": 5}))
 
 
 class HipEvents:
@@ -127,6 +141,9 @@ def cpu_baseline(wl, w_dev, x_dev, target_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)

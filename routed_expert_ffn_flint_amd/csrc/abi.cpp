@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/flint_moe.h"
 #include "launch.hpp"
 
@@ -43,6 +45,21 @@ flint_status check_T(const flint_moe_dims *d, int32_t T)
 
 int elem_bytes(const flint_moe_dims *d) { return d->dtype == FLINT_BF16 ? 2 : 4; }
 
+// Compute units of the current device, read once per device (the only state
+// the library keeps).  Falls back to 256 (MI355X) if the query fails.
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace
 
 namespace flint {
@@ -59,7 +76,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     Workspace w{};
     const size_t TK = (size_t)T * K;
     const int ntiles = (T + kTopkTile - 1) / kTopkTile;
-    const ExpertTiles tiles = expert_tiles_for(T);
+    const ExpertTiles tiles = expert_tiles_for(T, H, I, Is);
     const int cap1 = list_capacity(T, K, E, tiles.bm1);
     const int cap2 = list_capacity(T, K, E, tiles.bm2);
     size_t off = 0;
@@ -158,7 +175,7 @@ flint_status flint_moe_route(const flint_moe_dims *d, int32_t T, const void *x, 
 static DispatchArgs dispatch_args(const flint_moe_dims *d, int32_t T, const Workspace &w)
 {
     DispatchArgs a{};
-    const ExpertTiles tiles = expert_tiles_for(T);
+    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter);
     a.T = T;
     a.E = d->n_experts;
     a.K = d->top_k;
@@ -290,7 +307,8 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     e.y_shared = w.y_shared;
     e.out = out;
     e.out_bf16 = out_dtype == FLINT_BF16;
-    e.tiles = expert_tiles_for(T);
+    e.tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter);
+    e.grid_cap = 2 * device_cus();
     if (launch_experts(e, s, ev ? ev + 3 : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
     return FLINT_OK;
 }

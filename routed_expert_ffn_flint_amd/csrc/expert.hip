@@ -21,24 +21,52 @@
 
 namespace flint {
 
-template <bool SPLITK> struct WaveGrid;
-template <> struct WaveGrid<true> {   // 4 waves, same tile, k split in four
-    static constexpr int WM = 1, WN = 1;
+// Small-batch tile shapes (decode): rows per tile 32 (MB = 2 blocks of 16),
+// split-k over SPLIT waves.  Gate/up: NB/2 channels-blocks of 16 per tile;
+// down: NB column blocks of 16 per tile.
+#ifndef FLINT_GU_NB
+#define FLINT_GU_NB 4
+#endif
+#ifndef FLINT_GU_SPLIT
+#define FLINT_GU_SPLIT 4
+#endif
+#ifndef FLINT_GU_UNROLL
+#define FLINT_GU_UNROLL 4
+#endif
+#ifndef FLINT_DN_NB
+#define FLINT_DN_NB 4
+#endif
+#ifndef FLINT_DN_SPLIT
+#define FLINT_DN_SPLIT 4
+#endif
+#ifndef FLINT_DN_UNROLL
+#define FLINT_DN_UNROLL 4
+#endif
+#ifndef FLINT_GU_PIPE
+#define FLINT_GU_PIPE false
+#endif
+#ifndef FLINT_DN_PIPE
+#define FLINT_DN_PIPE false
+#endif
+
+template <int SPLIT> struct WaveGrid {  // SPLIT waves, same tile, k split SPLIT ways
+    static constexpr int WM = 1, WN = 1, THREADS = SPLIT * 64;
 };
-template <> struct WaveGrid<false> {  // 4 waves in a 2x2 grid, all of k each
-    static constexpr int WM = 2, WN = 2;
+template <> struct WaveGrid<1> {  // 4 waves in a 2x2 grid, all of k each
+    static constexpr int WM = 2, WN = 2, THREADS = 256;
 };
 
 // ---------------------------------------------------------------------------
 // Gate/up + SwiGLU.  A wave's NB column blocks are NB/2 gate blocks and the NB/2
 // up blocks of the same channels, so silu(g)*u pairs up in registers.
-template <typename DT, int MB, int NB, bool SPLITK>
-__global__ __launch_bounds__(256) void k_gate_up(ExpertArgs a, int n_shared_items)
+template <typename DT, int MB, int NB, int SPLIT, int U, bool PIPE>
+__global__ __launch_bounds__(WaveGrid<SPLIT>::THREADS) void k_gate_up(ExpertArgs a, int n_shared_items)
 {
     using S = typename DT::storage;
-    constexpr int WM = WaveGrid<SPLITK>::WM, WN = WaveGrid<SPLITK>::WN;
+    constexpr bool SPLITK = SPLIT > 1;
+    constexpr int WM = WaveGrid<SPLIT>::WM, WN = WaveGrid<SPLIT>::WN;
     constexpr int BM = WM * MB * 16, HALF = NB / 2, BN = WN * HALF * 16;
-    __shared__ float red[SPLITK ? 4 * MB * NB * 256 : 1];
+    __shared__ float red[SPLITK ? SPLIT * MB * NB * 256 : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = SPLITK ? 0 : wave / WN, wn = SPLITK ? 0 : wave % WN;
@@ -47,15 +75,13 @@ __global__ __launch_bounds__(256) void k_gate_up(ExpertArgs a, int n_shared_item
 
     int item = blockIdx.x;
     const bool shared = item < n_shared_items;
-    int width, row0, row_end, n0;
+    int width, row0, n0, e = -1, row_end = a.T;
     const S *wg, *wu;
     S *hout;
-    const int32_t *gather = nullptr;
     if (shared) {
         const int ntn = a.Is / BN;
         row0 = (item / ntn) * BM;
         n0 = (item % ntn) * BN;
-        row_end = a.T;
         width = a.Is;
         wg = (const S *)a.shared_gate;
         wu = (const S *)a.shared_up;
@@ -64,28 +90,20 @@ __global__ __launch_bounds__(256) void k_gate_up(ExpertArgs a, int n_shared_item
         item -= n_shared_items;
         const int ntn = a.I / BN;
         const int entry = item / ntn;
-        if (entry >= a.meta[0]) return;
-        const int e = a.list1[2 * entry];
+        const int nlist = a.meta[0];
+        e = a.list1[2 * entry];  // inside the list's capacity; used only if entry < nlist
         row0 = a.list1[2 * entry + 1];
+        if (entry >= nlist) return;
         row_end = a.offsets[e + 1];
         n0 = (item % ntn) * BN;
         width = a.I;
         wg = (const S *)a.gate + (size_t)e * a.I * H;
         wu = (const S *)a.up + (size_t)e * a.I * H;
         hout = (S *)a.h_sorted;
-        gather = a.sorted_token;
     }
 
     const int kg = (lane >> 4) * 8;
     const int rbase = row0 + wm * MB * 16;
-    const S *a_rows[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        int r = rbase + m * 16 + (lane & 15);
-        if (r >= row_end) r = row0;
-        const int tok = gather ? gather[r] : r;
-        a_rows[m] = x + (size_t)tok * H + kg;
-    }
     const int cbase = n0 + wn * HALF * 16;
     const S *b_rows[NB];
 #pragma unroll
@@ -94,22 +112,33 @@ __global__ __launch_bounds__(256) void k_gate_up(ExpertArgs a, int n_shared_item
         b_rows[j] = wg + (size_t)c * H + kg;
         b_rows[j + HALF] = wu + (size_t)c * H + kg;
     }
+    // A rows: routed rows are gathered token rows; rows past the tile's end
+    // repeat its first row (cache hits; their results are never stored)
+    auto resolve_a = [&](const S *(&a_rows)[MB]) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            int r = rbase + m * 16 + (lane & 15);
+            if (r >= row_end) r = row0;
+            const int tok = shared ? r : a.sorted_token[r];
+            a_rows[m] = x + (size_t)tok * H + kg;
+        }
+    };
 
     f32x4 acc[MB][NB];
     zero_acc(acc);
     const int nslices = H / 32;
     int s0 = 0, s1 = nslices;
     if (SPLITK) {
-        const int per = (nslices + 3) / 4;
+        const int per = (nslices + SPLIT - 1) / SPLIT;
         s0 = min(wave * per, nslices);
         s1 = min(s0 + per, nslices);
     }
-    wave_gemm<DT, MB, NB, 4>(a_rows, b_rows, s0, s1, acc);
-    if (SPLITK) splitk_reduce4(acc, red);
+    wave_gemm_stream<DT, MB, NB, U, PIPE>(resolve_a, b_rows, s0, s1, acc);
+    if (SPLITK) splitk_reduce<SPLIT, MB, NB>(acc, red);
 
 #pragma unroll
     for (int j = 0; j < HALF; ++j) {
-        if (SPLITK && (j % 4) != wave) continue;  // spread the stores over the waves
+        if (SPLITK && (j % SPLIT) != wave) continue;  // spread the stores over the waves
         const int c = cbase + j * 16 + (lane & 15);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
@@ -124,13 +153,14 @@ __global__ __launch_bounds__(256) void k_gate_up(ExpertArgs a, int n_shared_item
 
 // ---------------------------------------------------------------------------
 // Down projection: y[row][n] = down[n] . h[row], float32 out.
-template <typename DT, int MB, int NB, bool SPLITK>
-__global__ __launch_bounds__(256) void k_down(ExpertArgs a, int n_shared_items)
+template <typename DT, int MB, int NB, int SPLIT, int U, bool PIPE>
+__global__ __launch_bounds__(WaveGrid<SPLIT>::THREADS) void k_down(ExpertArgs a, int n_shared_items)
 {
     using S = typename DT::storage;
-    constexpr int WM = WaveGrid<SPLITK>::WM, WN = WaveGrid<SPLITK>::WN;
+    constexpr bool SPLITK = SPLIT > 1;
+    constexpr int WM = WaveGrid<SPLIT>::WM, WN = WaveGrid<SPLIT>::WN;
     constexpr int BM = WM * MB * 16, BN = WN * NB * 16;
-    __shared__ float red[SPLITK ? 4 * MB * NB * 256 : 1];
+    __shared__ float red[SPLITK ? SPLIT * MB * NB * 256 : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = SPLITK ? 0 : wave / WN, wn = SPLITK ? 0 : wave % WN;
@@ -139,13 +169,12 @@ __global__ __launch_bounds__(256) void k_down(ExpertArgs a, int n_shared_items)
 
     int item = blockIdx.x;
     const bool shared = item < n_shared_items;
-    int kdim, row0, row_end, n0;
+    int kdim, row0, n0, e = -1, row_end = a.T;
     const S *hin, *wd;
     float *yout;
     if (shared) {
         row0 = (item / ntn) * BM;
         n0 = (item % ntn) * BN;
-        row_end = a.T;
         kdim = a.Is;
         hin = (const S *)a.h_shared;
         wd = (const S *)a.shared_down;
@@ -153,9 +182,10 @@ __global__ __launch_bounds__(256) void k_down(ExpertArgs a, int n_shared_items)
     } else {
         item -= n_shared_items;
         const int entry = item / ntn;
-        if (entry >= a.meta[1]) return;
-        const int e = a.list2[2 * entry];
+        const int nlist = a.meta[1];
+        e = a.list2[2 * entry];
         row0 = a.list2[2 * entry + 1];
+        if (entry >= nlist) return;
         row_end = a.offsets[e + 1];
         n0 = (item % ntn) * BN;
         kdim = a.I;
@@ -166,13 +196,6 @@ __global__ __launch_bounds__(256) void k_down(ExpertArgs a, int n_shared_items)
 
     const int kg = (lane >> 4) * 8;
     const int rbase = row0 + wm * MB * 16;
-    const S *a_rows[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        int r = rbase + m * 16 + (lane & 15);
-        if (r >= row_end) r = row0;
-        a_rows[m] = hin + (size_t)r * kdim + kg;
-    }
     const int cbase = n0 + wn * NB * 16;
     const S *b_rows[NB];
 #pragma unroll
@@ -181,22 +204,30 @@ __global__ __launch_bounds__(256) void k_down(ExpertArgs a, int n_shared_items)
         if (c >= H) c = 0;
         b_rows[n] = wd + (size_t)c * kdim + kg;
     }
+    auto resolve_a = [&](const S *(&a_rows)[MB]) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            int r = rbase + m * 16 + (lane & 15);
+            if (r >= row_end) r = row0;
+            a_rows[m] = hin + (size_t)r * kdim + kg;
+        }
+    };
 
     f32x4 acc[MB][NB];
     zero_acc(acc);
     const int nslices = kdim / 32;
     int s0 = 0, s1 = nslices;
     if (SPLITK) {
-        const int per = (nslices + 3) / 4;
+        const int per = (nslices + SPLIT - 1) / SPLIT;
         s0 = min(wave * per, nslices);
         s1 = min(s0 + per, nslices);
     }
-    wave_gemm<DT, MB, NB, 4>(a_rows, b_rows, s0, s1, acc);
-    if (SPLITK) splitk_reduce4(acc, red);
+    wave_gemm_stream<DT, MB, NB, U, PIPE>(resolve_a, b_rows, s0, s1, acc);
+    if (SPLITK) splitk_reduce<SPLIT, MB, NB>(acc, red);
 
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-        if (SPLITK && (n % 4) != wave) continue;
+        if (SPLITK && (n % SPLIT) != wave) continue;
         const int c = cbase + n * 16 + (lane & 15);
         if (c >= H) continue;
 #pragma unroll
@@ -215,6 +246,8 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 {
     const int t = blockIdx.x;
     const int H = a.H, K = a.K;
+    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+    if (c >= H) return;
     int slots[kMaxTopK];
     float w[kMaxTopK];
 #pragma unroll
@@ -222,50 +255,62 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
         slots[k] = k < K ? a.slot_of[(size_t)t * K + k] : 0;
         w[k] = k < K ? a.topk_w[(size_t)t * K + k] : 0.f;
     }
-    for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            if (k < K) {
-                const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
-                acc[0] += w[k] * y[0];
-                acc[1] += w[k] * y[1];
-                acc[2] += w[k] * y[2];
-                acc[3] += w[k] * y[3];
-            }
+    for (int k = 0; k < kMaxTopK; ++k) {
+        if (k < K) {
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
+            acc[0] += w[k] * y[0];
+            acc[1] += w[k] * y[1];
+            acc[2] += w[k] * y[2];
+            acc[3] += w[k] * y[3];
         }
-        if (a.Is > 0) {
-            const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c);
-            acc[0] += y[0];
-            acc[1] += y[1];
-            acc[2] += y[2];
-            acc[3] += y[3];
-        }
-        if (a.out_bf16) {
-            uint16_t *o = (uint16_t *)a.out + (size_t)t * H + c;
-            o[0] = f32_to_bf16(acc[0]);
-            o[1] = f32_to_bf16(acc[1]);
-            o[2] = f32_to_bf16(acc[2]);
-            o[3] = f32_to_bf16(acc[3]);
-        } else {
-            *reinterpret_cast<f32x4 *>((float *)a.out + (size_t)t * H + c) = acc;
-        }
+    }
+    if (a.Is > 0) {
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c);
+        acc[0] += y[0];
+        acc[1] += y[1];
+        acc[2] += y[2];
+        acc[3] += y[3];
+    }
+    if (a.out_bf16) {
+        uint16_t *o = (uint16_t *)a.out + (size_t)t * H + c;
+        o[0] = f32_to_bf16(acc[0]);
+        o[1] = f32_to_bf16(acc[1]);
+        o[2] = f32_to_bf16(acc[2]);
+        o[3] = f32_to_bf16(acc[3]);
+    } else {
+        *reinterpret_cast<f32x4 *>((float *)a.out + (size_t)t * H + c) = acc;
     }
 }
 
 // ---------------------------------------------------------------------------
-ExpertTiles expert_tiles_for(int T)
+#ifndef FLINT_USE_STREAM
+#define FLINT_USE_STREAM 1
+#endif
+
+ExpertTiles expert_tiles_for(int T, int H, int I, int Is)
 {
+    if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
+        return ExpertTiles{stream_bm1(), 0, stream_bm2(), 0, true, true};
     // Small batches (decode): split-k kernels over 32-row tiles, so that one
     // tile holds every row an expert gets and each weight is read once.
-    if (T <= 512) return ExpertTiles{32, 32, 32, 64, true};
-    return ExpertTiles{128, 64, 128, 128, false};
+    if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false};
+    return ExpertTiles{128, 64, 128, 128, false, false};
 }
 
 template <typename DT>
 static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev)
 {
     const ExpertTiles &t = a.tiles;
+    if (t.stream) {
+        const hipError_t err = launch_experts_stream(a, a.grid_cap, stream, ev);
+        if (err != hipSuccess) return err;
+        if (ev) (void)hipEventRecord(ev[1], stream);
+        k_combine<<<dim3(a.T, (a.H + 1023) / 1024), 256, 0, stream>>>(a);
+        if (ev) (void)hipEventRecord(ev[2], stream);
+        return hipGetLastError();
+    }
     const int cap1 = list_capacity(a.T, a.K, a.E, t.bm1);
     const int cap2 = list_capacity(a.T, a.K, a.E, t.bm2);
     const int mt1 = (a.T + t.bm1 - 1) / t.bm1, mt2 = (a.T + t.bm2 - 1) / t.bm2;
@@ -274,16 +319,18 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, hipE
     const int g1 = ns1 + cap1 * (a.I / t.bn1);
     const int g2 = ns2 + cap2 * ((a.H + t.bn2 - 1) / t.bn2);
     if (t.small)
-        k_gate_up<DT, 2, 4, true><<<g1, 256, 0, stream>>>(a, ns1);
+        k_gate_up<DT, 2, FLINT_GU_NB, FLINT_GU_SPLIT, FLINT_GU_UNROLL, FLINT_GU_PIPE>
+            <<<g1, WaveGrid<FLINT_GU_SPLIT>::THREADS, 0, stream>>>(a, ns1);
     else
-        k_gate_up<DT, 4, 4, false><<<g1, 256, 0, stream>>>(a, ns1);
+        k_gate_up<DT, 4, 4, 1, 4, false><<<g1, 256, 0, stream>>>(a, ns1);
     if (ev) (void)hipEventRecord(ev[0], stream);
     if (t.small)
-        k_down<DT, 2, 4, true><<<g2, 256, 0, stream>>>(a, ns2);
+        k_down<DT, 2, FLINT_DN_NB, FLINT_DN_SPLIT, FLINT_DN_UNROLL, FLINT_DN_PIPE>
+            <<<g2, WaveGrid<FLINT_DN_SPLIT>::THREADS, 0, stream>>>(a, ns2);
     else
-        k_down<DT, 4, 4, false><<<g2, 256, 0, stream>>>(a, ns2);
+        k_down<DT, 4, 4, 1, 4, false><<<g2, 256, 0, stream>>>(a, ns2);
     if (ev) (void)hipEventRecord(ev[1], stream);
-    k_combine<<<a.T, 256, 0, stream>>>(a);
+    k_combine<<<dim3(a.T, (a.H + 1023) / 1024), 256, 0, stream>>>(a);
     if (ev) (void)hipEventRecord(ev[2], stream);
     return hipGetLastError();
 }

@@ -12,6 +12,8 @@ constexpr int kTopkTile = 256;
 // Maximum supported sizes.
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
+// Largest batch served by the persistent weight-streaming expert kernels.
+constexpr int kStreamMaxT = 512;
 
 // Tile shapes of the expert kernels for one launch regime.
 struct ExpertTiles {
@@ -19,10 +21,13 @@ struct ExpertTiles {
     int bn1;  // intermediate channels per gate/up tile
     int bm2;  // rows per down tile
     int bn2;  // output columns per down tile
-    bool small;  // split-k decode kernels (true) or tiled kernels (false)
+    bool small;   // split-k decode kernels (true) or tiled kernels (false)
+    bool stream;  // small batches on the persistent weight-streaming kernels
 };
 
-ExpertTiles expert_tiles_for(int T);
+// Tile shapes (and with them the dispatch's tile lists) for T tokens of a
+// layer with these sizes.
+ExpertTiles expert_tiles_for(int T, int H, int I, int Is);
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
@@ -86,9 +91,17 @@ struct ExpertArgs {
     void *out;
     bool out_bf16;
     ExpertTiles tiles;
+    int grid_cap;  // work-groups for the persistent kernels (from the device's CU count)
 };
 // stage_events (nullable): 3 events recorded after gate/up, down and combine.
 hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
+
+// Persistent streaming kernels (small batches, shapes whose H, I, Is split into
+// whole batches); grid_cap: work-groups to launch at most (a few per CU).
+bool stream_eligible(int T, int H, int I, int Is);
+int stream_bm1();
+int stream_bm2();
+hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, hipEvent_t const *ev);
 
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream);
 

@@ -26,20 +26,22 @@
 namespace flint {
 
 // ---------------------------------------------------------------------------
-// Router logits.  SPLITK: 4 waves compute the same 16x16 tile over quarters of
-// H (many small work-groups: the decode case, where reading the 1 MiB router
-// matrix quickly matters more than reuse).  Otherwise 4 waves in a 2x2 grid,
-// each (MB*16) tokens x (NB*16) experts over all of H.
-template <typename DT, int MB, int NB, bool SPLITK>
-__global__ __launch_bounds__(256) void k_router_logits(const typename DT::storage *__restrict__ x, int T, int H,
-                                                       const typename DT::storage *__restrict__ router,
-                                                       const float *__restrict__ bias, int E,
-                                                       float *__restrict__ z)
+// Router logits.  SPLIT > 1: SPLIT waves compute the same 16x16 tile over
+// slices of H and add their partial sums in wave order (many small
+// work-groups, each wave one batch of loads: the decode case, where the
+// latency of reading the 1 MiB router matrix matters more than reuse).
+// SPLIT == 1: 4 waves in a 2x2 grid, each (MB*16) tokens x (NB*16) experts
+// over all of H.
+template <typename DT, int MB, int NB, int SPLIT>
+__global__ __launch_bounds__(SPLIT > 1 ? SPLIT * 64 : 256) void k_router_logits(
+    const typename DT::storage *__restrict__ x, int T, int H, const typename DT::storage *__restrict__ router,
+    const float *__restrict__ bias, int E, float *__restrict__ z)
 {
     using S = typename DT::storage;
+    constexpr bool SPLITK = SPLIT > 1;
     constexpr int WM = SPLITK ? 1 : 2, WN = SPLITK ? 1 : 2;
     constexpr int TILE_T = WM * MB * 16, TILE_E = WN * NB * 16;
-    __shared__ float red[SPLITK ? 4 * MB * NB * 256 : 1];
+    __shared__ float red[SPLITK ? SPLIT * MB * NB * 256 : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = SPLITK ? 0 : wave / WN, wn = SPLITK ? 0 : wave % WN;
@@ -67,13 +69,13 @@ __global__ __launch_bounds__(256) void k_router_logits(const typename DT::storag
     const int nslices = H / 32;
     int s0 = 0, s1 = nslices;
     if (SPLITK) {
-        const int per = (nslices + 3) / 4;
+        const int per = (nslices + SPLIT - 1) / SPLIT;
         s0 = min(wave * per, nslices);
         s1 = min(s0 + per, nslices);
     }
     wave_gemm<DT, MB, NB, 4>(a_rows, b_rows, s0, s1, acc);
     if (SPLITK) {
-        splitk_reduce4(acc, red);
+        splitk_reduce<SPLIT, MB, NB>(acc, red);
         if (wave != 0) return;
     }
 #pragma unroll
@@ -96,20 +98,21 @@ hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const vo
 {
     if (T <= 0) return hipSuccess;
     if (T < 1024) {
+        // 16 waves per 16x16 tile, each wave 1/16 of H (at H = 2048: four 32-wide slices)
         dim3 grid((E + 15) / 16, (T + 15) / 16);
         if (bf16)
-            k_router_logits<BF16, 1, 1, true><<<grid, 256, 0, stream>>>(
+            k_router_logits<BF16, 1, 1, 16><<<grid, 1024, 0, stream>>>(
                 (const uint16_t *)x, T, H, (const uint16_t *)router, bias, E, logits);
         else
-            k_router_logits<F32, 1, 1, true><<<grid, 256, 0, stream>>>(
+            k_router_logits<F32, 1, 1, 16><<<grid, 1024, 0, stream>>>(
                 (const float *)x, T, H, (const float *)router, bias, E, logits);
     } else {
         dim3 grid((E + 127) / 128, (T + 63) / 64);
         if (bf16)
-            k_router_logits<BF16, 2, 4, false><<<grid, 256, 0, stream>>>(
+            k_router_logits<BF16, 2, 4, 1><<<grid, 256, 0, stream>>>(
                 (const uint16_t *)x, T, H, (const uint16_t *)router, bias, E, logits);
         else
-            k_router_logits<F32, 2, 4, false><<<grid, 256, 0, stream>>>(
+            k_router_logits<F32, 2, 4, 1><<<grid, 256, 0, stream>>>(
                 (const float *)x, T, H, (const float *)router, bias, E, logits);
     }
     return hipGetLastError();
@@ -173,95 +176,144 @@ __device__ void finish_offsets_and_lists(int c, int E, int32_t *offsets, int32_t
 
 __device__ __forceinline__ float score_from_logit(float z)
 {
-    // float32 score, rounded once from a double-precision sigmoid.
-    return (float)(1.0 / (1.0 + exp(-(double)z)));
+    return 1.0f / (1.0f + expf(-z));
 }
 
-// One work-group of 1024 threads per tile of 256 tokens.
-__global__ __launch_bounds__(1024) void k_topk_dispatch(DispatchArgs a, int fused_single_tile)
+// Selection key of a candidate: larger key = selected first.  Scores are
+// sigmoids (>= 0), whose float32 bit patterns order like the values, so the key
+// orders by score and then, for equal scores, by lower expert index.  Key 0 is
+// below every real candidate (used for experts past E and for padding).
+__device__ __forceinline__ uint64_t sel_key(float s, int e)
+{
+    return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
+__device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float((uint32_t)(k >> 32)); }
+
+__device__ __forceinline__ void cas_desc(uint64_t &a, uint64_t &b)
+{
+    const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+    a = hi;
+    b = lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off)
+{
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    return ((uint64_t)(uint32_t)__shfl_xor((int)hi, off, 64) << 32) | (uint32_t)__shfl_xor((int)lo, off, 64);
+}
+
+// Top-8 keys (descending) of one token, computed by a group of G lanes (G = 16
+// or 64): each lane sorts its 256/G candidates (experts gl + G*i) into a list
+// of the best 8, then log2(G) butterfly steps merge the lists across the group
+// -- the better half of two sorted lists is the element-wise larger of one list
+// and the other reversed (a bitonic sequence), which a 3-stage bitonic network
+// sorts.  Every lane of the group ends with the same list.
+template <int G>
+__device__ __forceinline__ void group_top8(const float *zt, int E, uint64_t (&l)[kMaxTopK])
+{
+    constexpr int C = kMaxExperts / G;
+    const int gl = threadIdx.x & (G - 1);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) l[j] = 0;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int e = gl + G * i;
+        uint64_t k = e < E ? sel_key(score_from_logit(zt[e]), e) : 0;
+        if (C <= kMaxTopK) {
+            l[i] = k;  // fewer candidates than list slots: keep all, sort below
+        } else if (k > l[kMaxTopK - 1]) {
+            l[kMaxTopK - 1] = k;
+#pragma unroll
+            for (int j = kMaxTopK - 1; j > 0; --j) cas_desc(l[j - 1], l[j]);
+        }
+    }
+    if (C <= kMaxTopK) {
+        // sort the C (<= 8) kept keys; padding keys are 0
+#pragma unroll
+        for (int i = 1; i < kMaxTopK; ++i)
+#pragma unroll
+            for (int j = i; j > 0; --j) cas_desc(l[j - 1], l[j]);
+    }
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) {
+        uint64_t p[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) p[j] = shfl_xor_u64(l[j], off);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) l[j] = l[j] > p[kMaxTopK - 1 - j] ? l[j] : p[kMaxTopK - 1 - j];
+#pragma unroll
+        for (int half = kMaxTopK / 2; half >= 1; half >>= 1)
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                if ((j & half) == 0) cas_desc(l[j], l[j + half]);
+    }
+}
+
+// Top-k for every token: groups of G lanes, one token per group, many
+// work-groups (the selection is arithmetic-heavy, so it is spread over the
+// whole chip).  Writes topk_idx (ascending expert ids) and topk_w.
+template <int G>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int K,
+                                              int32_t *__restrict__ topk_idx, float *__restrict__ topk_w)
+{
+    const int groups_per_block = blockDim.x / G;
+    const int tok = blockIdx.x * groups_per_block + threadIdx.x / G;
+    const int gl = threadIdx.x & (G - 1);
+    const int t = tok < T ? tok : T - 1;  // whole groups share a token; extra groups redo the last one
+    uint64_t l[kMaxTopK];
+    group_top8<G>(logits + (size_t)t * E, E, l);
+    if (tok >= T) return;
+    // the K best, in ascending expert order
+    int se[kMaxTopK];
+    float ss[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        se[k] = k < K ? key_expert(l[k]) : INT_MAX;
+        ss[k] = key_score(l[k]);
+    }
+#pragma unroll
+    for (int i = 1; i < kMaxTopK; ++i)
+#pragma unroll
+        for (int j = i; j > 0; --j)
+            if (se[j] < se[j - 1]) {
+                const int te = se[j];
+                se[j] = se[j - 1];
+                se[j - 1] = te;
+                const float ts = ss[j];
+                ss[j] = ss[j - 1];
+                ss[j - 1] = ts;
+            }
+    double sum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+        if (k < K) sum += (double)ss[k];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+        if (k < K && gl == k) {
+            topk_idx[(size_t)t * K + k] = se[k];
+            topk_w[(size_t)t * K + k] = (float)((double)ss[k] / sum);
+        }
+}
+
+// Dispatch of one tile of 256 tokens (1024 threads): a per-expert bitmask of
+// the tile's tokens gives each (token, expert) pair its rank among earlier
+// tokens of the tile, and the tile's per-expert histogram.  When the whole
+// batch is one tile the same work-group also scans the counts, scatters the
+// permutation and writes the expert kernels' tile lists.
+__global__ __launch_bounds__(1024) void k_dispatch_tile(DispatchArgs a, int fused_single_tile)
 {
     __shared__ int16_t sel[kTopkTile * kMaxTopK];
     __shared__ uint32_t masks[kMaxExperts * (kTopkTile / 32)];
     __shared__ int lds8[8];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int E = a.E, K = a.K;
     const int tile = blockIdx.x;
     const int t_base = tile * kTopkTile;
     const int tile_len = min(kTopkTile, a.T - t_base);
 
-    if (a.compute_topk) {
-        for (int tl = wave; tl < tile_len; tl += nwaves) {
-            const int t = t_base + tl;
-            const float *zt = a.logits + (size_t)t * E;
-            float s[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = lane + 64 * j;
-                s[j] = e < E ? score_from_logit(zt[e]) : -1.0f;
-            }
-            unsigned taken = 0;
-            int sel_e[kMaxTopK];
-            float sel_s[kMaxTopK];
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k) {
-                sel_e[k] = INT_MAX;
-                sel_s[k] = 0.f;
-                if (k < K) {
-                    float bs = -2.0f;
-                    int be = INT_MAX;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        // the lane's experts ascend with j, so strict '>' keeps the lower index
-                        if (!((taken >> j) & 1u) && s[j] > bs) {
-                            bs = s[j];
-                            be = lane + 64 * j;
-                        }
-                    }
-#pragma unroll
-                    for (int off = 32; off >= 1; off >>= 1) {
-                        const float os = __shfl_xor(bs, off, 64);
-                        const int oe = __shfl_xor(be, off, 64);
-                        if (os > bs || (os == bs && oe < be)) {
-                            bs = os;
-                            be = oe;
-                        }
-                    }
-                    sel_e[k] = be;
-                    sel_s[k] = bs;
-                    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-                }
-            }
-            // ascending expert order (K <= 8; every lane holds the same lists)
-#pragma unroll
-            for (int i = 1; i < kMaxTopK; ++i)
-#pragma unroll
-                for (int j = i; j > 0; --j)
-                    if (sel_e[j] < sel_e[j - 1]) {
-                        const int te = sel_e[j];
-                        sel_e[j] = sel_e[j - 1];
-                        sel_e[j - 1] = te;
-                        const float ts = sel_s[j];
-                        sel_s[j] = sel_s[j - 1];
-                        sel_s[j - 1] = ts;
-                    }
-            double sum = 0.0;
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k)
-                if (k < K) sum += (double)sel_s[k];
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k)
-                if (k < K && lane == k) {
-                    a.topk_idx[(size_t)t * K + k] = sel_e[k];
-                    a.topk_w[(size_t)t * K + k] = (float)((double)sel_s[k] / sum);
-                    sel[tl * K + k] = (int16_t)sel_e[k];
-                }
-        }
-    } else if (a.dispatch) {
-        for (int i = threadIdx.x; i < tile_len * K; i += blockDim.x)
-            sel[i] = (int16_t)a.topk_idx[(size_t)t_base * K + i];
-    }
-    if (!a.dispatch) return;
+    for (int i = threadIdx.x; i < tile_len * K; i += blockDim.x)
+        sel[i] = (int16_t)a.topk_idx[(size_t)t_base * K + i];
 
     constexpr int W = kTopkTile / 32;
     for (int i = threadIdx.x; i < E * W; i += blockDim.x) masks[i] = 0u;
@@ -367,15 +419,21 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream)
 
 hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream)
 {
-    if (a.T <= 0) {
-        return hipSuccess;
+    if (a.T <= 0) return hipSuccess;
+    if (a.compute_topk) {
+        if (a.T <= 1024)
+            k_topk<64><<<(a.T + 3) / 4, 256, 0, stream>>>(a.logits, a.T, a.E, a.K, a.topk_idx, a.topk_w);
+        else
+            k_topk<16><<<(a.T + 15) / 16, 256, 0, stream>>>(a.logits, a.T, a.E, a.K, a.topk_idx, a.topk_w);
     }
-    const int ntiles = (a.T + kTopkTile - 1) / kTopkTile;
-    const int fused = (ntiles == 1) ? 1 : 0;
-    k_topk_dispatch<<<ntiles, 1024, 0, stream>>>(a, fused);
-    if (a.dispatch && !fused) {
-        k_dispatch_scan<<<1, 256, 0, stream>>>(a, ntiles);
-        k_dispatch_scatter<<<(a.T * a.K + 255) / 256, 256, 0, stream>>>(a);
+    if (a.dispatch) {
+        const int ntiles = (a.T + kTopkTile - 1) / kTopkTile;
+        const int fused = (ntiles == 1) ? 1 : 0;
+        k_dispatch_tile<<<ntiles, 1024, 0, stream>>>(a, fused);
+        if (!fused) {
+            k_dispatch_scan<<<1, 256, 0, stream>>>(a, ntiles);
+            k_dispatch_scatter<<<(a.T * a.K + 255) / 256, 256, 0, stream>>>(a);
+        }
     }
     return hipGetLastError();
 }

@@ -1,0 +1,330 @@
+// Persistent weight-streaming expert kernels for small batches (decode).
+//
+// Layer (serving-kit review, "The architecture, from the config"; release news
+// page, "What runs on each token"): K selected experts of width I per token plus
+// an always-on shared expert of width Is, each a gated three-matrix SwiGLU.
+//
+// At decode batch sizes every selected expert holds a handful of rows, so the
+// layer is a stream of expert weights from HBM; the kernels here are built to
+// keep that stream full:
+//   - a fixed grid of work-groups (a few per CU) walks the work items with a
+//     static stride, so per-group setup is paid once, not per tile;
+//   - each work-group first copies the dispatch tables (tile list, expert
+//     offsets, the expert-sorted token list) into LDS, so looking up an item's
+//     expert, rows and tokens costs LDS reads only;
+//   - each wave streams its quarter of the reduction dimension in batches of U
+//     32-wide slices, the next batch (of this item or of the next one) issued
+//     before the current batch's MFMAs, so weight loads stay in flight across
+//     item boundaries;
+//   - the four waves' partial sums are added in LDS in wave order (the result
+//     does not depend on timing).
+// Gate/up items: 32 rows x (NB/2)*16 channels of gate and of up, SwiGLU fused.
+// Down items: 32 rows x NB*16 output columns.
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+#ifndef FLINT_ST_NB1
+#define FLINT_ST_NB1 4  // gate/up items: NB1/2 blocks of 16 channels
+#endif
+#ifndef FLINT_ST_NB2
+#define FLINT_ST_NB2 4  // down items: NB2 blocks of 16 columns
+#endif
+#ifndef FLINT_ST_UMAX1
+#define FLINT_ST_UMAX1 2  // gate/up slices per batch (register budget: 2 batches in flight)
+#endif
+#ifndef FLINT_ST_UMAX2
+#define FLINT_ST_UMAX2 2  // down slices per batch
+#endif
+#ifndef FLINT_ST_MB1
+#define FLINT_ST_MB1 2  // gate/up items: MB1 blocks of 16 rows
+#endif
+#ifndef FLINT_ST_MB2
+#define FLINT_ST_MB2 2  // down items: MB2 blocks of 16 rows
+#endif
+
+namespace flint {
+
+namespace {
+
+constexpr int kWaves = 4;
+
+// Dispatch tables in LDS: list (expert, first slot) pairs, offsets[E+1],
+// sorted_token[T*K] (gate/up only).
+struct Tables {
+    int32_t *list;
+    int32_t *offsets;
+    int32_t *sorted_token;
+    int nlist;
+};
+
+__device__ __forceinline__ Tables load_tables(const ExpertArgs &a, const int32_t *glist, int nlist, bool with_tokens,
+                                              int32_t *lds)
+{
+    Tables t;
+    t.nlist = nlist;
+    t.list = lds;
+    t.offsets = lds + 2 * nlist;
+    t.sorted_token = t.offsets + (a.E + 1);
+    for (int i = threadIdx.x; i < 2 * nlist; i += blockDim.x) t.list[i] = glist[i];
+    for (int i = threadIdx.x; i <= a.E; i += blockDim.x) t.offsets[i] = a.offsets[i];
+    if (with_tokens)
+        for (int i = threadIdx.x; i < a.T * a.K; i += blockDim.x) t.sorted_token[i] = a.sorted_token[i];
+    __syncthreads();
+    return t;
+}
+
+// What one wave needs for one work item.
+template <typename S, int MB, int NB>
+struct Item {
+    const S *a[MB];
+    const S *b[NB];
+    int s0;          // first slice of this wave
+    int nbatch;      // batches of U slices for this wave
+    int row0, row_end, n0, kdim;
+    int shared;      // 1: shared-expert item
+    int valid;
+};
+
+}  // namespace
+
+// GATE_UP: gate/up + SwiGLU -> h (dtype);  otherwise: down -> y (float32).
+template <typename DT, int MB, int NB, int U, bool GATE_UP>
+__global__ __launch_bounds__(256, 2) void k_expert_stream(ExpertArgs a, int n_shared_items)
+{
+    using S = typename DT::storage;
+    constexpr int BM = MB * 16;
+    constexpr int HALF = NB / 2;
+    constexpr int BN = GATE_UP ? HALF * 16 : NB * 16;  // channels (gate/up) or columns (down) per item
+    extern __shared__ int32_t dyn_lds[];
+    __shared__ float red[kWaves * MB * NB * 256];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kg = (lane >> 4) * 8;
+    const int H = a.H;
+    const int nlist = GATE_UP ? a.meta[0] : a.meta[1];
+    const Tables tab = load_tables(a, GATE_UP ? a.list1 : a.list2, nlist, GATE_UP, dyn_lds);
+
+    const int ntn_shared = GATE_UP ? a.Is / BN : (H + BN - 1) / BN;
+    const int ntn_routed = GATE_UP ? a.I / BN : (H + BN - 1) / BN;
+    const int n_items = n_shared_items + nlist * ntn_routed;
+
+    auto get = [&](int item) {
+        Item<S, MB, NB> it;
+        it.valid = item < n_items;
+        if (!it.valid) item = 0;  // a valid item's addresses, used only as dummy prefetch targets
+        int e = 0, nt;
+        const S *wa, *wb;  // gate/up (GATE_UP) or the down matrix (wa)
+        if (item < n_shared_items) {
+            it.shared = 1;
+            it.row0 = (item / ntn_shared) * BM;
+            nt = item % ntn_shared;
+            it.row_end = a.T;
+            it.kdim = GATE_UP ? H : a.Is;
+            wa = GATE_UP ? (const S *)a.shared_gate : (const S *)a.shared_down;
+            wb = (const S *)a.shared_up;
+        } else {
+            it.shared = 0;
+            const int r = item - n_shared_items;
+            const int entry = r / ntn_routed;
+            nt = r % ntn_routed;
+            e = tab.list[2 * entry];
+            it.row0 = tab.list[2 * entry + 1];
+            it.row_end = tab.offsets[e + 1];
+            it.kdim = GATE_UP ? H : a.I;
+            wa = GATE_UP ? (const S *)a.gate + (size_t)e * a.I * H : (const S *)a.down + (size_t)e * H * a.I;
+            wb = GATE_UP ? (const S *)a.up + (size_t)e * a.I * H : nullptr;
+        }
+        it.n0 = nt * BN;
+        const int per = it.kdim / 32 / kWaves;  // slices per wave (the launcher checks divisibility)
+        it.s0 = wave * per;
+        it.nbatch = per / U;
+        if (GATE_UP) {
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) {
+                const int c = it.n0 + j * 16 + (lane & 15);
+                it.b[j] = wa + (size_t)c * H + kg;
+                it.b[j + HALF] = wb + (size_t)c * H + kg;
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                int c = it.n0 + n * 16 + (lane & 15);
+                if (c >= H) c = 0;
+                it.b[n] = wa + (size_t)c * it.kdim + kg;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            int r = it.row0 + m * 16 + (lane & 15);
+            if (r >= it.row_end) r = it.row0;  // rows past the tile repeat its first row (cache hits)
+            if (GATE_UP) {
+                const int tok = it.shared ? r : tab.sorted_token[r];
+                it.a[m] = (const S *)a.x + (size_t)tok * H + kg;
+            } else {
+                it.a[m] = (it.shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * it.kdim + kg;
+            }
+        }
+        return it;
+    };
+
+    auto load_batch = [&](const Item<S, MB, NB> &it, int batch, Frag<DT> (&fb)[U][NB], Frag<DT> (&fa)[U][MB]) {
+        const int s = it.s0 + batch * U;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n) fb[u][n].load(it.b[n] + (s + u) * 32);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) fa[u][m].load(it.a[m] + (s + u) * 32);
+        }
+    };
+
+    // Two register buffers in ping-pong: while one batch is multiplied, the
+    // other batch's loads are in flight (each item has an even number of
+    // batches per wave, so item i's last batch always sits in buffer B and
+    // the next item's first batch goes to buffer A).
+    int item = blockIdx.x;
+    Item<S, MB, NB> cur = get(item);
+    if (!cur.valid) return;  // uniform across the work-group
+    Frag<DT> ab[U][NB], aa[U][MB], bb[U][NB], ba[U][MB];
+    load_batch(cur, 0, ab, aa);
+    while (true) {
+        const Item<S, MB, NB> nxt = get(item + gridDim.x);
+        f32x4 acc[MB][NB];
+        zero_acc(acc);
+        for (int j = 0; j < cur.nbatch; j += 2) {
+            // scheduling barriers keep each phase in program order, so that a
+            // buffer's loads are issued before the other buffer's MFMAs wait
+            load_batch(cur, j + 1, bb, ba);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) mma(acc[m][n], aa[u][m], ab[u][n]);
+            // buffer A: this item's batch j+2, else the next item's first batch
+            // (a dummy reload when there is no next item keeps the count of
+            // loads in flight fixed)
+            const bool more = j + 2 < cur.nbatch;
+            __builtin_amdgcn_sched_barrier(0);
+            load_batch(more ? cur : nxt, more ? j + 2 : 0, ab, aa);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) mma(acc[m][n], ba[u][m], bb[u][n]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        splitk_reduce<kWaves, MB, NB>(acc, red);
+        if (GATE_UP) {
+            S *hout = cur.shared ? (S *)a.h_shared : (S *)a.h_sorted;
+            const int width = cur.shared ? a.Is : a.I;
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) {
+                if ((j % kWaves) != wave) continue;
+                const int c = cur.n0 + j * 16 + (lane & 15);
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = cur.row0 + m * 16 + (lane >> 4) * 4 + i;
+                        if (r < cur.row_end)
+                            store_elem<DT>(hout + (size_t)r * width + c, swiglu(acc[m][j][i], acc[m][j + HALF][i]));
+                    }
+            }
+        } else {
+            float *yout = cur.shared ? a.y_shared : a.y_sorted;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                if ((n % kWaves) != wave) continue;
+                const int c = cur.n0 + n * 16 + (lane & 15);
+                if (c >= H) continue;
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = cur.row0 + m * 16 + (lane >> 4) * 4 + i;
+                        if (r < cur.row_end) yout[(size_t)r * H + c] = acc[m][n][i];
+                    }
+            }
+        }
+        __syncthreads();  // every wave has read `red` before the next item overwrites it
+        if (!nxt.valid) break;
+        cur = nxt;
+        item += gridDim.x;
+    }
+}
+
+// Eligible shapes: every item's reduction dimension splits evenly into 4 waves
+// x an even number of batches of U slices (gate/up: H; down: I and Is).
+static int unroll_for(const int *dims, int n, int umax)
+{
+    for (int U : {4, 2, 1}) {
+        if (U > umax) continue;
+        bool ok = true;
+        for (int i = 0; i < n; ++i) ok = ok && dims[i] % (32 * kWaves * U * 2) == 0;
+        if (ok) return U;
+    }
+    return 0;
+}
+static int unroll_gate_up(int H) { return unroll_for(&H, 1, FLINT_ST_UMAX1); }
+static int unroll_down(int I, int Is)
+{
+    const int d[2] = {I, Is > 0 ? Is : I};
+    return unroll_for(d, 2, FLINT_ST_UMAX2);
+}
+
+bool stream_eligible(int T, int H, int I, int Is)
+{
+    return T <= kStreamMaxT && unroll_gate_up(H) > 0 && unroll_down(I, Is) > 0;
+}
+int stream_bm1() { return FLINT_ST_MB1 * 16; }
+int stream_bm2() { return FLINT_ST_MB2 * 16; }
+
+template <typename DT, int U, bool GATE_UP>
+static void launch_one(const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream)
+{
+    if (GATE_UP)
+        k_expert_stream<DT, FLINT_ST_MB1, FLINT_ST_NB1, U, true><<<grid, 256, lds, stream>>>(a, n_shared);
+    else
+        k_expert_stream<DT, FLINT_ST_MB2, FLINT_ST_NB2, U, false><<<grid, 256, lds, stream>>>(a, n_shared);
+}
+
+template <typename DT, bool GATE_UP>
+static void launch_u(int U, const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream)
+{
+    if (U == 4) launch_one<DT, 4, GATE_UP>(a, grid, n_shared, lds, stream);
+    else if (U == 2) launch_one<DT, 2, GATE_UP>(a, grid, n_shared, lds, stream);
+    else launch_one<DT, 1, GATE_UP>(a, grid, n_shared, lds, stream);
+}
+
+template <typename DT>
+static void launch_stream_t(const ExpertArgs &a, int grid_cap, hipStream_t stream, hipEvent_t const *ev)
+{
+    const int bm1 = FLINT_ST_MB1 * 16, bm2 = FLINT_ST_MB2 * 16;
+    const int bn1 = FLINT_ST_NB1 / 2 * 16, bn2 = FLINT_ST_NB2 * 16;
+    const int cap1 = list_capacity(a.T, a.K, a.E, bm1);
+    const int cap2 = list_capacity(a.T, a.K, a.E, bm2);
+    const int ns1 = a.Is > 0 ? (a.T + bm1 - 1) / bm1 * (a.Is / bn1) : 0;
+    const int ns2 = a.Is > 0 ? (a.T + bm2 - 1) / bm2 * ((a.H + bn2 - 1) / bn2) : 0;
+    const int max1 = ns1 + cap1 * (a.I / bn1);
+    const int max2 = ns2 + cap2 * ((a.H + bn2 - 1) / bn2);
+    const size_t lds1 = (size_t)(2 * cap1 + a.E + 1 + a.T * a.K) * 4;
+    const size_t lds2 = (size_t)(2 * cap2 + a.E + 1) * 4;
+    launch_u<DT, true>(unroll_gate_up(a.H), a, min(grid_cap, max1), ns1, lds1, stream);
+    if (ev) (void)hipEventRecord(ev[0], stream);
+    launch_u<DT, false>(unroll_down(a.I, a.Is), a, min(grid_cap, max2), ns2, lds2, stream);
+}
+
+hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, hipEvent_t const *ev)
+{
+    if (a.bf16)
+        launch_stream_t<BF16>(a, grid_cap, stream, ev);
+    else
+        launch_stream_t<F32>(a, grid_cap, stream, ev);
+    return hipGetLastError();
+}
+
+}  // namespace flint

@@ -84,6 +84,19 @@ def test_decode32_every_token():
           f"distinct experts={len(np.unique(st['idx']))}")
 
 
+@pytest.mark.parametrize("T", [1, 5, 33, 200, 512, 513])
+def test_flint_layer_small_batches(T):
+    """Flint-shaped layer (H=2048, 256 experts top-6, 512/1024 wide) at batch
+    sizes around the decode kernels' range (up to 512 tokens; 513 takes the
+    tiled kernels): routing of every token, outputs of sampled tokens."""
+    wl = inputs.Workload(f"flint_T{T}", T, 2048, 256, 6, 512, 1024, True, 5)
+    w, x = _layer(wl)
+    sample = list(range(T)) if T <= 40 else list(np.random.default_rng(T).choice(T, 40, replace=False)) + [T - 1]
+    st = G.parity_sampled(wl, w, x, sample)
+    _check_dispatch_of(wl, st["idx"])
+    print(f"flint T={T}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
+
+
 def _check_dispatch_of(wl, gi):
     d = api.dims_of(wl)
     idx_dev = torch.from_numpy(gi).to("cuda")
