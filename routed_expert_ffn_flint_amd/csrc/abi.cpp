@@ -76,7 +76,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     Workspace w{};
     const size_t TK = (size_t)T * K;
     const int ntiles = (T + kTopkTile - 1) / kTopkTile;
-    const ExpertTiles tiles = expert_tiles_for(T, H, I, Is);
+    const ExpertTiles tiles = expert_tiles_for(T, H, I, Is, eb == 2);
     const int cap1 = list_capacity(T, K, E, tiles.bm1);
     const int cap2 = list_capacity(T, K, E, tiles.bm2);
     size_t off = 0;
@@ -175,7 +175,7 @@ flint_status flint_moe_route(const flint_moe_dims *d, int32_t T, const void *x, 
 static DispatchArgs dispatch_args(const flint_moe_dims *d, int32_t T, const Workspace &w)
 {
     DispatchArgs a{};
-    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter);
+    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter, d->dtype == FLINT_BF16);
     a.T = T;
     a.E = d->n_experts;
     a.K = d->top_k;
@@ -261,6 +261,7 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
                                  elem_bytes(d));
     hipEvent_t const *ev = (hipEvent_t const *)events;
+    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter, d->dtype == FLINT_BF16);
     if (ev && hipEventRecord(ev[0], s) != hipSuccess) return FLINT_DEVICE_ERROR;
     if (launch_router_logits(bf16, x, T, d->hidden, wt->router, wt->router_bias, d->n_experts, w.logits, s) !=
         hipSuccess)
@@ -307,8 +308,8 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     e.y_shared = w.y_shared;
     e.out = out;
     e.out_bf16 = out_dtype == FLINT_BF16;
-    e.tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter);
-    e.grid_cap = 2 * device_cus();
+    e.tiles = tiles;
+    e.grid_cap = stream_wgs_per_cu() * device_cus();
     if (launch_experts(e, s, ev ? ev + 3 : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
     return FLINT_OK;
 }

@@ -289,22 +289,24 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 #define FLINT_USE_STREAM 1
 #endif
 
-ExpertTiles expert_tiles_for(int T, int H, int I, int Is)
+ExpertTiles expert_tiles_for(int T, int H, int I, int Is, bool bf16)
 {
     if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
-        return ExpertTiles{stream_bm1(), 0, stream_bm2(), 0, true, true};
+        return ExpertTiles{stream_bm1(), 0, stream_bm2(), 0, true, true, false};
     // Small batches (decode): split-k kernels over 32-row tiles, so that one
     // tile holds every row an expert gets and each weight is read once.
-    if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false};
-    return ExpertTiles{128, 64, 128, 128, false, false};
+    if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};
+    if (tiled_eligible(H, I, Is, bf16)) return ExpertTiles{kTiledBM, 0, kTiledBM, 0, false, false, true};
+    return ExpertTiles{128, 64, 128, 128, false, false, false};
 }
 
 template <typename DT>
 static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev)
 {
     const ExpertTiles &t = a.tiles;
-    if (t.stream) {
-        const hipError_t err = launch_experts_stream(a, a.grid_cap, stream, ev);
+    if (t.stream || t.tiled) {
+        const hipError_t err =
+            t.stream ? launch_experts_stream(a, a.grid_cap, stream, ev) : launch_experts_tiled(a, stream, ev);
         if (err != hipSuccess) return err;
         if (ev) (void)hipEventRecord(ev[1], stream);
         k_combine<<<dim3(a.T, (a.H + 1023) / 1024), 256, 0, stream>>>(a);

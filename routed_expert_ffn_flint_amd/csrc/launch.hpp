@@ -23,11 +23,12 @@ struct ExpertTiles {
     int bn2;  // output columns per down tile
     bool small;   // split-k decode kernels (true) or tiled kernels (false)
     bool stream;  // small batches on the persistent weight-streaming kernels
+    bool tiled;   // large bf16 batches on the LDS-tiled kernels
 };
 
 // Tile shapes (and with them the dispatch's tile lists) for T tokens of a
 // layer with these sizes.
-ExpertTiles expert_tiles_for(int T, int H, int I, int Is);
+ExpertTiles expert_tiles_for(int T, int H, int I, int Is, bool bf16);
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
@@ -101,7 +102,13 @@ hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, hipEvent_t co
 bool stream_eligible(int T, int H, int I, int Is);
 int stream_bm1();
 int stream_bm2();
+int stream_wgs_per_cu();
 hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, hipEvent_t const *ev);
+
+// LDS-tiled kernels for large bf16 batches (128-row tiles).
+constexpr int kTiledBM = 128;
+bool tiled_eligible(int H, int I, int Is, bool bf16);
+hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev);
 
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream);
 

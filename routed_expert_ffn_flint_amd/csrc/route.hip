@@ -253,17 +253,84 @@ __device__ __forceinline__ void group_top8(const float *zt, int E, uint64_t (&l)
 // Top-k for every token: groups of G lanes, one token per group, many
 // work-groups (the selection is arithmetic-heavy, so it is spread over the
 // whole chip).  Writes topk_idx (ascending expert ids) and topk_w.
-template <int G>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int K,
-                                              int32_t *__restrict__ topk_idx, float *__restrict__ topk_w)
+// LDS of one tile's dispatch.
+struct TileLds {
+    int16_t sel[kTopkTile * kMaxTopK];
+    uint32_t masks[kMaxExperts * (kTopkTile / 32)];
+    int32_t offs[kMaxExperts];
+    int lds8[8];
+};
+
+// Dispatch of one tile of up to 256 tokens by a work-group of NT threads: a
+// per-expert bitmask of the tile's tokens gives each (token, expert) pair its
+// rank among earlier tokens of the tile (a popcount of the lower bits), and
+// the tile's per-expert histogram.  When the whole batch is one tile
+// (`single`) the same work-group also scans the counts, scatters the
+// permutation and writes the expert kernels' tile lists.
+template <int NT>
+__device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, TileLds &L)
 {
-    const int groups_per_block = blockDim.x / G;
-    const int tok = blockIdx.x * groups_per_block + threadIdx.x / G;
-    const int gl = threadIdx.x & (G - 1);
-    const int t = tok < T ? tok : T - 1;  // whole groups share a token; extra groups redo the last one
-    uint64_t l[kMaxTopK];
-    group_top8<G>(logits + (size_t)t * E, E, l);
-    if (tok >= T) return;
+    constexpr int PER = kTopkTile * kMaxTopK / NT;  // pairs per thread, at most
+    constexpr int W = kTopkTile / 32;
+    const int E = a.E, K = a.K;
+    const int t_base = tile * kTopkTile;
+    const int tile_len = min(kTopkTile, a.T - t_base);
+
+    for (int i = threadIdx.x; i < tile_len * K; i += NT) L.sel[i] = (int16_t)a.topk_idx[(size_t)t_base * K + i];
+    for (int i = threadIdx.x; i < E * W; i += NT) L.masks[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < tile_len * K; i += NT) {
+        const int tl = i / K, e = L.sel[i];
+        atomicOr(&L.masks[e * W + (tl >> 5)], 1u << (tl & 31));
+    }
+    __syncthreads();
+    int my_rank[PER];
+    int my_e[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int i = threadIdx.x + r * NT;
+        my_e[r] = -1;
+        my_rank[r] = 0;
+        if (i < tile_len * K) {
+            const int tl = i / K, e = L.sel[i];
+            int rk = __popc(L.masks[e * W + (tl >> 5)] & ((1u << (tl & 31)) - 1u));
+            for (int w = 0; w < (tl >> 5); ++w) rk += __popc(L.masks[e * W + w]);
+            my_rank[r] = rk;
+            my_e[r] = e;
+        }
+    }
+    int hcount = 0;
+    if (threadIdx.x < E)
+        for (int w = 0; w < W; ++w) hcount += __popc(L.masks[threadIdx.x * W + w]);
+
+    if (!single) {
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int i = threadIdx.x + r * NT;
+            if (my_e[r] >= 0) a.rank[(size_t)t_base * K + i] = my_rank[r];
+        }
+        if (threadIdx.x < E) a.hist[(size_t)tile * E + threadIdx.x] = hcount;
+        return;
+    }
+    finish_offsets_and_lists(hcount, E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2, a.meta, L.lds8);
+    if (threadIdx.x < E) L.offs[threadIdx.x] = a.offsets[threadIdx.x];  // this thread's own write
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int i = threadIdx.x + r * NT;
+        if (my_e[r] >= 0) {
+            const int slot = L.offs[my_e[r]] + my_rank[r];
+            a.sorted_token[slot] = t_base + i / K;
+            a.slot_of[(size_t)t_base * K + i] = slot;
+        }
+    }
+}
+
+// The K best keys of a token, written in ascending expert order with weights
+// s / sum(s) (the sum taken in double in that order); lane gl writes entry gl.
+__device__ __forceinline__ void write_topk(const uint64_t (&l)[kMaxTopK], int t, int K, int gl,
+                                           int32_t *__restrict__ topk_idx, float *__restrict__ topk_w)
+{
     // the K best, in ascending expert order
     int se[kMaxTopK];
     float ss[kMaxTopK];
@@ -296,78 +363,26 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
         }
 }
 
-// Dispatch of one tile of 256 tokens (1024 threads): a per-expert bitmask of
-// the tile's tokens gives each (token, expert) pair its rank among earlier
-// tokens of the tile, and the tile's per-expert histogram.  When the whole
-// batch is one tile the same work-group also scans the counts, scatters the
-// permutation and writes the expert kernels' tile lists.
+template <int G>
+__global__ __launch_bounds__(256) void k_topk(DispatchArgs da)
+{
+    const float *__restrict__ logits = da.logits;
+    const int T = da.T, E = da.E, K = da.K;
+    int32_t *__restrict__ topk_idx = da.topk_idx;
+    float *__restrict__ topk_w = da.topk_w;
+    const int groups_per_block = blockDim.x / G;
+    const int tok = blockIdx.x * groups_per_block + threadIdx.x / G;
+    const int gl = threadIdx.x & (G - 1);
+    const int t = tok < T ? tok : T - 1;  // whole groups share a token; extra groups redo the last one
+    uint64_t l[kMaxTopK];
+    group_top8<G>(logits + (size_t)t * E, E, l);
+    if (tok < T) write_topk(l, t, K, gl, topk_idx, topk_w);
+}
+
 __global__ __launch_bounds__(1024) void k_dispatch_tile(DispatchArgs a, int fused_single_tile)
 {
-    __shared__ int16_t sel[kTopkTile * kMaxTopK];
-    __shared__ uint32_t masks[kMaxExperts * (kTopkTile / 32)];
-    __shared__ int lds8[8];
-
-    const int E = a.E, K = a.K;
-    const int tile = blockIdx.x;
-    const int t_base = tile * kTopkTile;
-    const int tile_len = min(kTopkTile, a.T - t_base);
-
-    for (int i = threadIdx.x; i < tile_len * K; i += blockDim.x)
-        sel[i] = (int16_t)a.topk_idx[(size_t)t_base * K + i];
-
-    constexpr int W = kTopkTile / 32;
-    for (int i = threadIdx.x; i < E * W; i += blockDim.x) masks[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < tile_len * K; i += blockDim.x) {
-        const int tl = i / K, e = sel[i];
-        atomicOr(&masks[e * W + (tl >> 5)], 1u << (tl & 31));
-    }
-    __syncthreads();
-    // rank of each (token, expert) pair among the tile's earlier tokens of that expert
-    int my_rank[2];
-    int my_e[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int i = threadIdx.x + r * 1024;
-        my_e[r] = -1;
-        if (i < tile_len * K) {
-            const int tl = i / K, e = sel[i];
-            int rk = __popc(masks[e * W + (tl >> 5)] & ((1u << (tl & 31)) - 1u));
-            for (int w = 0; w < (tl >> 5); ++w) rk += __popc(masks[e * W + w]);
-            my_rank[r] = rk;
-            my_e[r] = e;
-        }
-    }
-    int hcount = 0;
-    if (threadIdx.x < E)
-        for (int w = 0; w < W; ++w) hcount += __popc(masks[threadIdx.x * W + w]);
-
-    if (!fused_single_tile) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int i = threadIdx.x + r * 1024;
-            if (my_e[r] >= 0) a.rank[(size_t)t_base * K + i] = my_rank[r];
-        }
-        if (threadIdx.x < E) a.hist[(size_t)tile * E + threadIdx.x] = hcount;
-        return;
-    }
-
-    // Single tile: finish the dispatch here.
-    __shared__ int32_t offs[kMaxExperts];
-    finish_offsets_and_lists(hcount, E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2,
-                             a.meta, lds8);
-    if (threadIdx.x < E) offs[threadIdx.x] = a.offsets[threadIdx.x];
-    // offsets were written by this block; re-read through LDS after a barrier
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int i = threadIdx.x + r * 1024;
-        if (my_e[r] >= 0) {
-            const int slot = offs[my_e[r]] + my_rank[r];
-            a.sorted_token[slot] = t_base + i / K;
-            a.slot_of[(size_t)t_base * K + i] = slot;
-        }
-    }
+    __shared__ TileLds L;
+    dispatch_tile<1024>(a, blockIdx.x, fused_single_tile != 0, L);
 }
 
 // More than one tile: per-expert column scan of the tile histograms.
@@ -420,14 +435,14 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream)
 hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream)
 {
     if (a.T <= 0) return hipSuccess;
+    const int ntiles = (a.T + kTopkTile - 1) / kTopkTile;
     if (a.compute_topk) {
         if (a.T <= 1024)
-            k_topk<64><<<(a.T + 3) / 4, 256, 0, stream>>>(a.logits, a.T, a.E, a.K, a.topk_idx, a.topk_w);
+            k_topk<64><<<(a.T + 3) / 4, 256, 0, stream>>>(a);
         else
-            k_topk<16><<<(a.T + 15) / 16, 256, 0, stream>>>(a.logits, a.T, a.E, a.K, a.topk_idx, a.topk_w);
+            k_topk<16><<<(a.T + 15) / 16, 256, 0, stream>>>(a);
     }
     if (a.dispatch) {
-        const int ntiles = (a.T + kTopkTile - 1) / kTopkTile;
         const int fused = (ntiles == 1) ? 1 : 0;
         k_dispatch_tile<<<ntiles, 1024, 0, stream>>>(a, fused);
         if (!fused) {

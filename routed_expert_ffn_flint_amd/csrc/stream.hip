@@ -27,7 +27,7 @@
 #define FLINT_ST_NB1 4  // gate/up items: NB1/2 blocks of 16 channels
 #endif
 #ifndef FLINT_ST_NB2
-#define FLINT_ST_NB2 4  // down items: NB2 blocks of 16 columns
+#define FLINT_ST_NB2 2  // down items: NB2 blocks of 16 columns
 #endif
 #ifndef FLINT_ST_UMAX1
 #define FLINT_ST_UMAX1 2  // gate/up slices per batch (register budget: 2 batches in flight)
@@ -38,6 +38,10 @@
 #ifndef FLINT_ST_MB1
 #define FLINT_ST_MB1 2  // gate/up items: MB1 blocks of 16 rows
 #endif
+#ifndef FLINT_ST_WGS
+#define FLINT_ST_WGS 2  // resident work-groups per CU (register and LDS budget)
+#endif
+
 #ifndef FLINT_ST_MB2
 #define FLINT_ST_MB2 2  // down items: MB2 blocks of 16 rows
 #endif
@@ -89,7 +93,7 @@ struct Item {
 
 // GATE_UP: gate/up + SwiGLU -> h (dtype);  otherwise: down -> y (float32).
 template <typename DT, int MB, int NB, int U, bool GATE_UP>
-__global__ __launch_bounds__(256, 2) void k_expert_stream(ExpertArgs a, int n_shared_items)
+__global__ __launch_bounds__(256, FLINT_ST_WGS) void k_expert_stream(ExpertArgs a, int n_shared_items)
 {
     using S = typename DT::storage;
     constexpr int BM = MB * 16;
@@ -282,6 +286,7 @@ bool stream_eligible(int T, int H, int I, int Is)
 }
 int stream_bm1() { return FLINT_ST_MB1 * 16; }
 int stream_bm2() { return FLINT_ST_MB2 * 16; }
+int stream_wgs_per_cu() { return FLINT_ST_WGS; }
 
 template <typename DT, int U, bool GATE_UP>
 static void launch_one(const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream)
