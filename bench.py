@@ -12,9 +12,14 @@ last-level cache cannot serve repeated weight reads.
 
 Prints ONE JSON line.  Beside the headline throughput:
   roofline      the dominant kernel's algorithmic bytes (or flops) per launch
-                over its mean launch duration, from HIP events recorded around
-                it on the library's stream during a second pass of the same
-                steps, against MI355X's published peak;
+                over its mean launch duration, from HIP events that the library
+                stamps at that kernel's own begin and end (hipExtLaunchKernel,
+                on the library's stream) during a second pass of the same
+                steps, against MI355X's published peak; `traffic` is the HBM
+                bytes per launch that the committed rocprofv3 counter summary
+                for this kernel and workload records (FETCH_SIZE + WRITE_SIZE,
+                scaled by the same counters on a plain copy), or null when the
+                kernel's sources have changed since it was taken;
   cpu_baseline  the oracle (plain fp64 C) timed on the host on a bounded
                 sample of the same workload.
 """
@@ -22,8 +27,10 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +39,14 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s (bf16, H=2048, 256e top-6) + % HBM/MFMA roofline"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "routed_expert_ffn_flint_amd", "csrc")
+# the sources each gate/up kernel is built from
+KERNEL_SOURCES = {
+    "k_expert_stream": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream.hip"],
+    "k_tiled": ["common.hpp", "gemm_core.hpp", "launch.hpp", "tiled.hip"],
+}
+STREAM_MAX_T = 512  # largest batch the library serves with the streaming kernels
 
 
 def parse():
@@ -91,6 +106,30 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(e)
+
+
+def sources_digest(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def counters_traffic(kernel, workload, digest):
+    """HBM bytes per launch from profiles/<kernel>_gate_up.<workload>.hbm_counters.md
+    (its json block), if that summary was taken on these very sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_gate_up.{workload}.hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        m = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha256") != digest:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
 
 
 def algorithmic(wl, idx_np):
@@ -180,7 +219,7 @@ def main():
         if events is None:
             st = lib.flint_moe_forward(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp, wsp, wsn, sp)
         else:
-            arr = (ctypes.c_void_p * 6)(*[e.value for e in events])
+            arr = (ctypes.c_void_p * 10)(*[e.value for e in events])
             st = lib.flint_moe_forward_profiled(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp,
                                                 wsp, wsn, sp, arr)
         if st != 0:
@@ -263,11 +302,12 @@ def main():
     ms = start.elapsed_time(end) / steps_done
     tokens_per_s = T / (ms / 1e3)
 
-    # ---- per-stage timing pass (events on the library's stream) -------------
+    # ---- per-stage timing pass: start/stop events stamped at the stages' own
+    # first-kernel begin and last-kernel end, on the library's stream ---------
     hev = HipEvents()
     n_prof = min(args.steps, 100)
     n_layers_step = n_copies if stack else 1
-    ev_sets = [[hev.create(6) for _ in range(n_layers_step)] for _ in range(n_prof)]
+    ev_sets = [[hev.create(10) for _ in range(n_layers_step)] for _ in range(n_prof)]
     for i in range(n_prof):
         step(i, ev_sets[i])
     torch.cuda.synchronize()
@@ -276,7 +316,7 @@ def main():
     for i in range(n_prof):
         for evs in ev_sets[i]:
             for j, n in enumerate(names):
-                stage[n].append(hev.ms(evs[j], evs[j + 1]))
+                stage[n].append(hev.ms(evs[2 * j], evs[2 * j + 1]))
     for sets in ev_sets:
         for evs in sets:
             hev.destroy(evs)
@@ -289,18 +329,21 @@ def main():
     layer_flops = float(np.mean([p["flops"]["layer"] for p in per_copy]))
     gu_flops = float(np.mean([p["flops"]["gate_up"] for p in per_copy]))
     big = T >= 2048
+    kernel = "k_expert_stream" if T <= STREAM_MAX_T else "k_tiled"
+    digest = sources_digest(kernel)
+    traffic = counters_traffic(kernel, wl.name, digest)
+    kname = f"{kernel}<gate/up> (grouped gate/up GEMM + SwiGLU, routed and shared)"
     if big:
         achieved = gu_flops / (stage_us["gate_up"] * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": "k_gate_up (grouped gate/up GEMM + SwiGLU)",
-                    "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                    "per_launch": {"flops": gu_flops, "mean_us": stage_us["gate_up"]}}
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic, "kernel": kname,
+                    "per_launch": {"flops": gu_flops, "bytes": gate_up_bytes, "mean_us": stage_us["gate_up"]}}
     else:
         achieved = gate_up_bytes / (stage_us["gate_up"] * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "kernel": "k_gate_up (grouped gate/up GEMM + SwiGLU)",
-                    "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kname,
                     "per_launch": {"bytes": gate_up_bytes, "mean_us": stage_us["gate_up"]}}
+    roofline["sources_sha256"] = digest
     layer_time_s = ms / 1e3 / (n_copies if stack else 1)
     layer = {"hbm_GBs": layer_bytes / layer_time_s / 1e9,
              "hbm_frac": layer_bytes / layer_time_s / 1e9 / HBM_PEAK_GBS,

@@ -146,11 +146,14 @@ flint_status flint_moe_forward(const flint_moe_dims *dims, int32_t T, const void
                                float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
 
 /* flint_moe_forward with stage timing: identical arguments, results and
- * kernels, plus `events`, an array of 6 hipEvent_t handles (created by the
- * caller, passed as void*) that are recorded on `stream` before the router and
- * after each stage: [0] start, [1] router logits, [2] top-k and dispatch,
- * [3] gate/up + SwiGLU, [4] down projection, [5] combine.  The caller reads
- * them with hipEventElapsedTime.  NULL `events` makes it flint_moe_forward. */
+ * kernels, plus `events`, an array of 10 hipEvent_t handles (created by the
+ * caller, passed as void*): a start and a stop event for each of the five
+ * stages, in the order router logits, top-k + dispatch, gate/up + SwiGLU, down
+ * projection, combine ([2i] start, [2i+1] stop of stage i).  The kernels are
+ * launched with hipExtLaunchKernel, so a stage's start is stamped when its
+ * first kernel begins and its stop when its last kernel ends: the interval is
+ * kernel execution time, as a kernel trace reports it.  The caller reads them
+ * with hipEventElapsedTime.  NULL `events` makes it flint_moe_forward. */
 flint_status flint_moe_forward_profiled(const flint_moe_dims *dims, int32_t T, const void *x,
                                         const flint_moe_weights *weights, void *out,
                                         flint_dtype out_dtype, int32_t *topk_idx_out,

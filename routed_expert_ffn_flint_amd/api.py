@@ -125,8 +125,12 @@ def weights_struct(d: Dims, w: dict) -> Weights:
                    g("shared_gate"), g("shared_up"), g("shared_down"))
 
 
-def flint_moe_forward(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=None, ws=None, stream=None):
-    """weights: a dict of tensors (see inputs.make_layer) or a prepared Weights struct."""
+def flint_moe_forward(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=None, ws=None, stream=None,
+                      events=None):
+    """weights: a dict of tensors (see inputs.make_layer) or a prepared Weights struct.
+    events: None, or 10 hipEvent_t handles (ints / c_void_p) -- then the call goes
+    to flint_moe_forward_profiled, which stamps a start and a stop event around
+    each of the five stages."""
     T = x.shape[0]
     _check_tensor("x", x, _elem(d), (T, d.hidden))
     if out.dtype not in (torch.float32, torch.bfloat16):
@@ -137,11 +141,17 @@ def flint_moe_forward(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=No
     _check_tensor("ws", ws, torch.uint8)
     ws_struct = weights if isinstance(weights, Weights) else weights_struct(d, weights)
     out_dt = BF16 if out.dtype == torch.bfloat16 else F32
-    st = load().flint_moe_forward(ctypes.byref(d), T, _ptr(x), ctypes.byref(ws_struct), _ptr(out), out_dt,
-                                  _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws),
-                                  0 if ws is None else ws.numel(), _stream(stream))
+    args = (ctypes.byref(d), T, _ptr(x), ctypes.byref(ws_struct), _ptr(out), out_dt, _ptr(topk_idx_out),
+            _ptr(topk_w_out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if events is None:
+        st = load().flint_moe_forward(*args)
+    else:
+        if len(events) != 10:
+            raise ValueError("events: 10 hipEvent_t handles (start/stop of 5 stages)")
+        arr = (ctypes.c_void_p * 10)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
+        st = load().flint_moe_forward_profiled(*args, arr)
     if st != OK:
-        raise FlintError(st, "flint_moe_forward")
+        raise FlintError(st, "flint_moe_forward" if events is None else "flint_moe_forward_profiled")
 
 
 def flint_rmsnorm(inp, out, eps=1e-6, stream=None):

@@ -260,11 +260,13 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     const bool bf16 = d->dtype == FLINT_BF16;
     Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
                                  elem_bytes(d));
-    hipEvent_t const *ev = (hipEvent_t const *)events;
+    // stage marks: router, top-k + dispatch, gate/up, down, combine
+    Marks marks[5];
+    if (events)
+        for (int i = 0; i < 5; ++i) marks[i] = Marks{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]};
     const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter, d->dtype == FLINT_BF16);
-    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return FLINT_DEVICE_ERROR;
-    if (launch_router_logits(bf16, x, T, d->hidden, wt->router, wt->router_bias, d->n_experts, w.logits, s) !=
-        hipSuccess)
+    if (launch_router_logits(bf16, x, T, d->hidden, wt->router, wt->router_bias, d->n_experts, w.logits, s,
+                             marks[0]) != hipSuccess)
         return FLINT_DEVICE_ERROR;
 
     DispatchArgs a = dispatch_args(d, T, w);
@@ -276,9 +278,7 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     a.offsets = w.offsets;
     a.sorted_token = w.sorted_token;
     a.slot_of = w.slot_of;
-    if (ev && hipEventRecord(ev[1], s) != hipSuccess) return FLINT_DEVICE_ERROR;
-    if (launch_topk_dispatch(a, s) != hipSuccess) return FLINT_DEVICE_ERROR;
-    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return FLINT_DEVICE_ERROR;
+    if (launch_topk_dispatch(a, s, marks[1]) != hipSuccess) return FLINT_DEVICE_ERROR;
 
     ExpertArgs e{};
     e.bf16 = bf16;
@@ -310,7 +310,7 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     e.out_bf16 = out_dtype == FLINT_BF16;
     e.tiles = tiles;
     e.grid_cap = stream_wgs_per_cu() * device_cus();
-    if (launch_experts(e, s, ev ? ev + 3 : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
+    if (launch_experts(e, s, events ? marks + 2 : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
     return FLINT_OK;
 }
 

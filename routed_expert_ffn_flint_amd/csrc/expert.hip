@@ -301,17 +301,16 @@ ExpertTiles expert_tiles_for(int T, int H, int I, int Is, bool bf16)
 }
 
 template <typename DT>
-static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev)
+static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
     const ExpertTiles &t = a.tiles;
+    const Marks m1 = marks ? marks[0] : Marks{}, m2 = marks ? marks[1] : Marks{}, m3 = marks ? marks[2] : Marks{};
+    const dim3 gc(a.T, (a.H + 1023) / 1024);
     if (t.stream || t.tiled) {
         const hipError_t err =
-            t.stream ? launch_experts_stream(a, a.grid_cap, stream, ev) : launch_experts_tiled(a, stream, ev);
+            t.stream ? launch_experts_stream(a, a.grid_cap, stream, marks) : launch_experts_tiled(a, stream, marks);
         if (err != hipSuccess) return err;
-        if (ev) (void)hipEventRecord(ev[1], stream);
-        k_combine<<<dim3(a.T, (a.H + 1023) / 1024), 256, 0, stream>>>(a);
-        if (ev) (void)hipEventRecord(ev[2], stream);
-        return hipGetLastError();
+        return launch_k(k_combine, gc, 256, 0, stream, m3, a);
     }
     const int cap1 = list_capacity(a.T, a.K, a.E, t.bm1);
     const int cap2 = list_capacity(a.T, a.K, a.E, t.bm2);
@@ -320,27 +319,26 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, hipE
     const int ns2 = a.Is > 0 ? mt2 * ((a.H + t.bn2 - 1) / t.bn2) : 0;
     const int g1 = ns1 + cap1 * (a.I / t.bn1);
     const int g2 = ns2 + cap2 * ((a.H + t.bn2 - 1) / t.bn2);
+    hipError_t err;
     if (t.small)
-        k_gate_up<DT, 2, FLINT_GU_NB, FLINT_GU_SPLIT, FLINT_GU_UNROLL, FLINT_GU_PIPE>
-            <<<g1, WaveGrid<FLINT_GU_SPLIT>::THREADS, 0, stream>>>(a, ns1);
+        err = launch_k(k_gate_up<DT, 2, FLINT_GU_NB, FLINT_GU_SPLIT, FLINT_GU_UNROLL, FLINT_GU_PIPE>, g1,
+                       WaveGrid<FLINT_GU_SPLIT>::THREADS, 0, stream, m1, a, ns1);
     else
-        k_gate_up<DT, 4, 4, 1, 4, false><<<g1, 256, 0, stream>>>(a, ns1);
-    if (ev) (void)hipEventRecord(ev[0], stream);
+        err = launch_k(k_gate_up<DT, 4, 4, 1, 4, false>, g1, 256, 0, stream, m1, a, ns1);
+    if (err != hipSuccess) return err;
     if (t.small)
-        k_down<DT, 2, FLINT_DN_NB, FLINT_DN_SPLIT, FLINT_DN_UNROLL, FLINT_DN_PIPE>
-            <<<g2, WaveGrid<FLINT_DN_SPLIT>::THREADS, 0, stream>>>(a, ns2);
+        err = launch_k(k_down<DT, 2, FLINT_DN_NB, FLINT_DN_SPLIT, FLINT_DN_UNROLL, FLINT_DN_PIPE>, g2,
+                       WaveGrid<FLINT_DN_SPLIT>::THREADS, 0, stream, m2, a, ns2);
     else
-        k_down<DT, 4, 4, 1, 4, false><<<g2, 256, 0, stream>>>(a, ns2);
-    if (ev) (void)hipEventRecord(ev[1], stream);
-    k_combine<<<dim3(a.T, (a.H + 1023) / 1024), 256, 0, stream>>>(a);
-    if (ev) (void)hipEventRecord(ev[2], stream);
-    return hipGetLastError();
+        err = launch_k(k_down<DT, 4, 4, 1, 4, false>, g2, 256, 0, stream, m2, a, ns2);
+    if (err != hipSuccess) return err;
+    return launch_k(k_combine, gc, 256, 0, stream, m3, a);
 }
 
-hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev)
+hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
     if (a.T <= 0) return hipSuccess;
-    return a.bf16 ? launch_experts_t<BF16>(a, stream, ev) : launch_experts_t<F32>(a, stream, ev);
+    return a.bf16 ? launch_experts_t<BF16>(a, stream, marks) : launch_experts_t<F32>(a, stream, marks);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,11 +1,43 @@
 // Host-side launch interface between the C ABI (abi.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace flint {
+
+// Timing marks of one stage (either may be null).  A kernel launched through
+// launch_k with a non-null mark has it stamped by the runtime when that kernel
+// itself begins (start) or ends (stop), so a stage's interval is its kernels'
+// execution time, without the queue gaps around them.
+struct Marks {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// kernel<<<grid, block, lds, s>>>(args...), through hipExtLaunchKernel when a
+// mark is given.  Returns hipGetLastError() / the launch status.
+template <typename... P, typename... A>
+hipError_t launch_k(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, Marks m, A &&...args)
+{
+    if (!m.start && !m.stop) {
+        kernel<<<grid, block, lds, s>>>(std::forward<A>(args)...);
+        return hipGetLastError();
+    }
+    std::tuple<P...> vals{std::forward<A>(args)...};
+    void *ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
+    std::apply(
+        [&ptrs](auto &...v) {
+            int i = 0;
+            ((ptrs[i++] = (void *)&v), ...);
+        },
+        vals);
+    return hipExtLaunchKernel((const void *)kernel, grid, block, ptrs, lds, s, m.start, m.stop, 0);
+}
 
 // Tokens per work-group in the top-k / dispatch kernels.
 constexpr int kTopkTile = 256;
@@ -61,7 +93,7 @@ int list_capacity(int T, int K, int E, int bm);
 
 // logits[t][e] = x[t] . router[e] (+ bias[e]), float32.
 hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const void *router,
-                                const float *bias, int E, float *logits, hipStream_t stream);
+                                const float *bias, int E, float *logits, hipStream_t stream, Marks m = {});
 
 // Top-k selection and/or dispatch.  See route.hip for the modes.
 struct DispatchArgs {
@@ -76,7 +108,7 @@ struct DispatchArgs {
     int32_t *list1, *list2, *meta;
     int bm1, bm2;
 };
-hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream);
+hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks m = {});
 
 struct ExpertArgs {
     bool bf16;
@@ -94,8 +126,8 @@ struct ExpertArgs {
     ExpertTiles tiles;
     int grid_cap;  // work-groups for the persistent kernels (from the device's CU count)
 };
-// stage_events (nullable): 3 events recorded after gate/up, down and combine.
-hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
+// marks (nullable): 3 stages, gate/up (+ shared), down (+ shared), combine.
+hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 
 // Persistent streaming kernels (small batches, shapes whose H, I, Is split into
 // whole batches); grid_cap: work-groups to launch at most (a few per CU).
@@ -103,12 +135,13 @@ bool stream_eligible(int T, int H, int I, int Is);
 int stream_bm1();
 int stream_bm2();
 int stream_wgs_per_cu();
-hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, hipEvent_t const *ev);
+// marks (nullable): gate/up and down stages.
+hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, const Marks *marks);
 
 // LDS-tiled kernels for large bf16 batches (128-row tiles).
 constexpr int kTiledBM = 128;
 bool tiled_eligible(int H, int I, int Is, bool bf16);
-hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev);
+hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream);
 

@@ -94,28 +94,20 @@ __global__ __launch_bounds__(SPLIT > 1 ? SPLIT * 64 : 256) void k_router_logits(
 }
 
 hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const void *router,
-                                const float *bias, int E, float *logits, hipStream_t stream)
+                                const float *bias, int E, float *logits, hipStream_t stream, Marks m)
 {
     if (T <= 0) return hipSuccess;
+    const uint16_t *xb = (const uint16_t *)x, *rb = (const uint16_t *)router;
+    const float *xf = (const float *)x, *rf = (const float *)router;
     if (T < 1024) {
         // 16 waves per 16x16 tile, each wave 1/16 of H (at H = 2048: four 32-wide slices)
         dim3 grid((E + 15) / 16, (T + 15) / 16);
-        if (bf16)
-            k_router_logits<BF16, 1, 1, 16><<<grid, 1024, 0, stream>>>(
-                (const uint16_t *)x, T, H, (const uint16_t *)router, bias, E, logits);
-        else
-            k_router_logits<F32, 1, 1, 16><<<grid, 1024, 0, stream>>>(
-                (const float *)x, T, H, (const float *)router, bias, E, logits);
-    } else {
-        dim3 grid((E + 127) / 128, (T + 63) / 64);
-        if (bf16)
-            k_router_logits<BF16, 2, 4, 1><<<grid, 256, 0, stream>>>(
-                (const uint16_t *)x, T, H, (const uint16_t *)router, bias, E, logits);
-        else
-            k_router_logits<F32, 2, 4, 1><<<grid, 256, 0, stream>>>(
-                (const float *)x, T, H, (const float *)router, bias, E, logits);
+        if (bf16) return launch_k(k_router_logits<BF16, 1, 1, 16>, grid, 1024, 0, stream, m, xb, T, H, rb, bias, E, logits);
+        return launch_k(k_router_logits<F32, 1, 1, 16>, grid, 1024, 0, stream, m, xf, T, H, rf, bias, E, logits);
     }
-    return hipGetLastError();
+    dim3 grid((E + 127) / 128, (T + 63) / 64);
+    if (bf16) return launch_k(k_router_logits<BF16, 2, 4, 1>, grid, 256, 0, stream, m, xb, T, H, rb, bias, E, logits);
+    return launch_k(k_router_logits<F32, 2, 4, 1>, grid, 256, 0, stream, m, xf, T, H, rf, bias, E, logits);
 }
 
 // ---------------------------------------------------------------------------
@@ -432,25 +424,29 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream)
+hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks m)
 {
     if (a.T <= 0) return hipSuccess;
     const int ntiles = (a.T + kTopkTile - 1) / kTopkTile;
+    const int fused = (ntiles == 1) ? 1 : 0;
+    // the first kernel carries m.start, the last m.stop
+    Marks first{m.start, a.dispatch ? nullptr : m.stop};
+    hipError_t err = hipSuccess;
     if (a.compute_topk) {
-        if (a.T <= 1024)
-            k_topk<64><<<(a.T + 3) / 4, 256, 0, stream>>>(a);
-        else
-            k_topk<16><<<(a.T + 15) / 16, 256, 0, stream>>>(a);
+        err = a.T <= 1024 ? launch_k(k_topk<64>, (a.T + 3) / 4, 256, 0, stream, first, a)
+                          : launch_k(k_topk<16>, (a.T + 15) / 16, 256, 0, stream, first, a);
+        if (err != hipSuccess) return err;
+        first.start = nullptr;
     }
     if (a.dispatch) {
-        const int fused = (ntiles == 1) ? 1 : 0;
-        k_dispatch_tile<<<ntiles, 1024, 0, stream>>>(a, fused);
-        if (!fused) {
-            k_dispatch_scan<<<1, 256, 0, stream>>>(a, ntiles);
-            k_dispatch_scatter<<<(a.T * a.K + 255) / 256, 256, 0, stream>>>(a);
-        }
+        err = launch_k(k_dispatch_tile, ntiles, 1024, 0, stream, Marks{first.start, fused ? m.stop : nullptr}, a,
+                       fused);
+        if (err != hipSuccess || fused) return err;
+        err = launch_k(k_dispatch_scan, 1, 256, 0, stream, Marks{}, a, ntiles);
+        if (err != hipSuccess) return err;
+        err = launch_k(k_dispatch_scatter, (a.T * a.K + 255) / 256, 256, 0, stream, Marks{nullptr, m.stop}, a);
     }
-    return hipGetLastError();
+    return err;
 }
 
 }  // namespace flint

@@ -289,24 +289,25 @@ int stream_bm2() { return FLINT_ST_MB2 * 16; }
 int stream_wgs_per_cu() { return FLINT_ST_WGS; }
 
 template <typename DT, int U, bool GATE_UP>
-static void launch_one(const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream)
+static hipError_t launch_one(const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream, Marks m)
 {
     if (GATE_UP)
-        k_expert_stream<DT, FLINT_ST_MB1, FLINT_ST_NB1, U, true><<<grid, 256, lds, stream>>>(a, n_shared);
-    else
-        k_expert_stream<DT, FLINT_ST_MB2, FLINT_ST_NB2, U, false><<<grid, 256, lds, stream>>>(a, n_shared);
+        return launch_k(k_expert_stream<DT, FLINT_ST_MB1, FLINT_ST_NB1, U, true>, grid, 256, lds, stream, m, a,
+                        n_shared);
+    return launch_k(k_expert_stream<DT, FLINT_ST_MB2, FLINT_ST_NB2, U, false>, grid, 256, lds, stream, m, a, n_shared);
 }
 
 template <typename DT, bool GATE_UP>
-static void launch_u(int U, const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream)
+static hipError_t launch_u(int U, const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream,
+                           Marks m)
 {
-    if (U == 4) launch_one<DT, 4, GATE_UP>(a, grid, n_shared, lds, stream);
-    else if (U == 2) launch_one<DT, 2, GATE_UP>(a, grid, n_shared, lds, stream);
-    else launch_one<DT, 1, GATE_UP>(a, grid, n_shared, lds, stream);
+    if (U == 4) return launch_one<DT, 4, GATE_UP>(a, grid, n_shared, lds, stream, m);
+    if (U == 2) return launch_one<DT, 2, GATE_UP>(a, grid, n_shared, lds, stream, m);
+    return launch_one<DT, 1, GATE_UP>(a, grid, n_shared, lds, stream, m);
 }
 
 template <typename DT>
-static void launch_stream_t(const ExpertArgs &a, int grid_cap, hipStream_t stream, hipEvent_t const *ev)
+static hipError_t launch_stream_t(const ExpertArgs &a, int grid_cap, hipStream_t stream, const Marks *marks)
 {
     const int bm1 = FLINT_ST_MB1 * 16, bm2 = FLINT_ST_MB2 * 16;
     const int bn1 = FLINT_ST_NB1 / 2 * 16, bn2 = FLINT_ST_NB2 * 16;
@@ -318,18 +319,16 @@ static void launch_stream_t(const ExpertArgs &a, int grid_cap, hipStream_t strea
     const int max2 = ns2 + cap2 * ((a.H + bn2 - 1) / bn2);
     const size_t lds1 = (size_t)(2 * cap1 + a.E + 1 + a.T * a.K) * 4;
     const size_t lds2 = (size_t)(2 * cap2 + a.E + 1) * 4;
-    launch_u<DT, true>(unroll_gate_up(a.H), a, min(grid_cap, max1), ns1, lds1, stream);
-    if (ev) (void)hipEventRecord(ev[0], stream);
-    launch_u<DT, false>(unroll_down(a.I, a.Is), a, min(grid_cap, max2), ns2, lds2, stream);
+    const hipError_t err = launch_u<DT, true>(unroll_gate_up(a.H), a, min(grid_cap, max1), ns1, lds1, stream,
+                                              marks ? marks[0] : Marks{});
+    if (err != hipSuccess) return err;
+    return launch_u<DT, false>(unroll_down(a.I, a.Is), a, min(grid_cap, max2), ns2, lds2, stream,
+                               marks ? marks[1] : Marks{});
 }
 
-hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, hipEvent_t const *ev)
+hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, const Marks *marks)
 {
-    if (a.bf16)
-        launch_stream_t<BF16>(a, grid_cap, stream, ev);
-    else
-        launch_stream_t<F32>(a, grid_cap, stream, ev);
-    return hipGetLastError();
+    return a.bf16 ? launch_stream_t<BF16>(a, grid_cap, stream, marks) : launch_stream_t<F32>(a, grid_cap, stream, marks);
 }
 
 }  // namespace flint

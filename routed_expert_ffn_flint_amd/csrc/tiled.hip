@@ -195,7 +195,7 @@ bool tiled_eligible(int H, int I, int Is, bool bf16)
     return bf16 && H % TBK == 0 && I % 64 == 0 && Is % 64 == 0;
 }
 
-hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, hipEvent_t const *ev)
+hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
     const int cap1 = list_capacity(a.T, a.K, a.E, TBM);
     const int cap2 = cap1;
@@ -205,10 +205,9 @@ hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, hipEven
     auto round8 = [](int g) { return (g + kXcds - 1) / kXcds * kXcds; };
     const int g1 = round8(ns1 + cap1 * (a.I / (TBN / 2)));
     const int g2 = round8(ns2 + cap2 * ((a.H + TBN - 1) / TBN));
-    k_tiled<true><<<g1, 256, 0, stream>>>(a, ns1);
-    if (ev) (void)hipEventRecord(ev[0], stream);
-    k_tiled<false><<<g2, 256, 0, stream>>>(a, ns2);
-    return hipGetLastError();
+    const hipError_t err = launch_k(k_tiled<true>, g1, 256, 0, stream, marks ? marks[0] : Marks{}, a, ns1);
+    if (err != hipSuccess) return err;
+    return launch_k(k_tiled<false>, g2, 256, 0, stream, marks ? marks[1] : Marks{}, a, ns2);
 }
 
 }  // namespace flint

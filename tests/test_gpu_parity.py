@@ -211,3 +211,55 @@ def test_rmsnorm_matches_oracle():
     eps = float(np.float32(1e-6))
     got = api.rmsnorm(y.to("cuda"), eps).float().cpu().numpy()
     np.testing.assert_array_equal(got, orc.rmsnorm(y.numpy(), eps))
+
+
+PROFILED = ["decode32", "prefill4096"]
+
+
+@pytest.mark.parametrize("name", PROFILED)
+def test_profiled_forward_same_bits_and_ordered_stages(name):
+    """flint_moe_forward_profiled runs the same kernels as flint_moe_forward (same
+    bits out) and stamps five disjoint, ordered stage intervals that fit inside
+    the call's own span on the stream."""
+    import ctypes
+    wl = inputs.WORKLOADS[name]
+    w, x = _layer(wl)
+    d = api.dims_of(wl)
+    a, ia, wa = G.gpu_layer(wl, w, x)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(12):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e)
+    T = wl.T
+    out = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, wl.top_k), dtype=torch.float32, device="cuda")
+    ws = api.workspace(d, T)
+    stream = torch.cuda.current_stream()
+    assert hip.hipEventRecord(evs[10], ctypes.c_void_p(stream.cuda_stream)) == 0
+    api.flint_moe_forward(d, x, w, out, idx, tw, ws, stream, events=evs[:10])
+    assert hip.hipEventRecord(evs[11], ctypes.c_void_p(stream.cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(ia, idx) and torch.equal(wa, tw)
+    assert torch.equal(a.view(torch.int32), out.view(torch.int32))
+
+    def ms(i, j):
+        v = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(v), evs[i], evs[j]) == 0
+        return v.value
+
+    stages = [ms(2 * s, 2 * s + 1) for s in range(5)]
+    assert all(t > 0 for t in stages), stages
+    # each stage starts after the previous one stopped
+    for s in range(4):
+        assert ms(2 * s + 1, 2 * s + 2) >= 0
+    total = ms(10, 11)
+    assert sum(stages) <= total * 1.001 + 1e-3, (stages, total)
+    print(f"{name}: stages_us={[round(t * 1e3, 1) for t in stages]} span_us={total * 1e3:.1f}")
+    for e in evs:
+        hip.hipEventDestroy(e)
