@@ -76,7 +76,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     Workspace w{};
     const size_t TK = (size_t)T * K;
     const int ntiles = (T + kTopkTile - 1) / kTopkTile;
-    const ExpertTiles tiles = expert_tiles_for(T, H, I, Is, eb == 2);
+    const ExpertTiles tiles = expert_tiles_for(T, H, E, K, I, Is, eb == 2);
     const int cap1 = list_capacity(T, K, E, tiles.bm1);
     const int cap2 = list_capacity(T, K, E, tiles.bm2);
     size_t off = 0;
@@ -175,7 +175,8 @@ flint_status flint_moe_route(const flint_moe_dims *d, int32_t T, const void *x, 
 static DispatchArgs dispatch_args(const flint_moe_dims *d, int32_t T, const Workspace &w)
 {
     DispatchArgs a{};
-    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter, d->dtype == FLINT_BF16);
+    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                                               d->dtype == FLINT_BF16);
     a.T = T;
     a.E = d->n_experts;
     a.K = d->top_k;
@@ -264,7 +265,8 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     Marks marks[5];
     if (events)
         for (int i = 0; i < 5; ++i) marks[i] = Marks{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]};
-    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->inter, d->shared_inter, d->dtype == FLINT_BF16);
+    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                                               d->dtype == FLINT_BF16);
     if (launch_router_logits(bf16, x, T, d->hidden, wt->router, wt->router_bias, d->n_experts, w.logits, s,
                              marks[0]) != hipSuccess)
         return FLINT_DEVICE_ERROR;

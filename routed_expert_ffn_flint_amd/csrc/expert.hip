@@ -289,14 +289,15 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 #define FLINT_USE_STREAM 1
 #endif
 
-ExpertTiles expert_tiles_for(int T, int H, int I, int Is, bool bf16)
+ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf16)
 {
     if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
         return ExpertTiles{stream_bm1(), 0, stream_bm2(), 0, true, true, false};
     // Small batches (decode): split-k kernels over 32-row tiles, so that one
     // tile holds every row an expert gets and each weight is read once.
     if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};
-    if (tiled_eligible(H, I, Is, bf16)) return ExpertTiles{kTiledBM, 0, kTiledBM, 0, false, false, true};
+    if (tiled_eligible(T, K, E, H, I, Is, bf16))
+        return ExpertTiles{tiled_bm1(T, K, E), 0, tiled_bm2(T, K, E), 0, false, false, true};
     return ExpertTiles{128, 64, 128, 128, false, false, false};
 }
 

@@ -60,7 +60,7 @@ struct ExpertTiles {
 
 // Tile shapes (and with them the dispatch's tile lists) for T tokens of a
 // layer with these sizes.
-ExpertTiles expert_tiles_for(int T, int H, int I, int Is, bool bf16);
+ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf16);
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
@@ -138,10 +138,16 @@ int stream_wgs_per_cu();
 // marks (nullable): gate/up and down stages.
 hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, const Marks *marks);
 
-// LDS-tiled kernels for large bf16 batches (128-row tiles).
-constexpr int kTiledBM = 128;
-bool tiled_eligible(int H, int I, int Is, bool bf16);
+// LDS-tiled kernels for large bf16 batches: rows per gate/up and per down tile
+// (128 or 256, from the mean rows per expert), eligibility, launch.
+int tiled_bm1(int T, int K, int E);
+int tiled_bm2(int T, int K, int E);
+bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16);
 hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
+// The router product on the same tiles (large bf16 batches).
+bool tiled_router_eligible(int T, int H, bool bf16);
+hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
+                               float *logits, hipStream_t stream, Marks m);
 
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream);
 

@@ -97,6 +97,7 @@ hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const vo
                                 const float *bias, int E, float *logits, hipStream_t stream, Marks m)
 {
     if (T <= 0) return hipSuccess;
+    if (tiled_router_eligible(T, H, bf16)) return launch_router_tiled(x, T, H, router, bias, E, logits, stream, m);
     const uint16_t *xb = (const uint16_t *)x, *rb = (const uint16_t *)router;
     const float *xf = (const float *)x, *rf = (const float *)router;
     if (T < 1024) {

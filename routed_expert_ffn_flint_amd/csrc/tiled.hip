@@ -1,26 +1,40 @@
-// LDS-tiled grouped GEMMs for large batches (prefill).
+// LDS-tiled GEMMs for large batches (prefill): the grouped expert products and
+// the router.
 //
 // Layer (serving-kit review, "The architecture, from the config"; release news
-// page, "What runs on each token"): K selected experts of width I per token plus
-// an always-on shared expert of width Is, each a gated three-matrix SwiGLU.
+// page, "What runs on each token"): a sigmoid router over the experts, then K
+// selected experts of width I per token plus an always-on shared expert of
+// width Is, each a gated three-matrix SwiGLU.
 //
-// With hundreds of rows per expert the expert products are real GEMMs, so
+// With hundreds of rows per expert the expert products are real GEMMs, so both
 // operands are staged through LDS and reused:
-//   - a work-group computes a 128 x 128 tile (4 waves in 2 x 2, 64 x 64 each,
-//     16x16x32 bf16 MFMAs) over k in slices of 64, double-buffered in LDS:
-//     the next slice's global loads are in flight while the current slice's
-//     MFMAs run;
-//   - gate/up tiles hold 64 gate rows and the 64 up rows of the same channels;
-//     each wave's columns are 32 gate + the 32 matching up channels, so
-//     silu(g) * u is formed in registers;
-//   - LDS rows are padded to a 144-byte pitch, which makes the 16-row fragment
-//     reads conflict-free;
+//   - a work-group computes a BM x BN output tile; its waves each own a
+//     WM x WN block built from 16x16x32 bf16 MFMAs; k runs in slices of 64;
+//   - operands go from global memory straight into LDS
+//     (global_load_lds_dwordx4: lane l of a wave's load lands at the
+//     instruction's LDS base + 16 l), so no registers hold them in flight and
+//     no LDS write instructions are issued;
+//   - a stage holds the tile's BM A rows then its BN B rows, 128 bytes each
+//     (one 64-element slice).  The 16-byte chunk c of row r is stored at chunk
+//     position c ^ (r & 7): each load instruction covers 8 whole rows (every
+//     row one 128-byte global segment), and a fragment read -- 16 rows, one
+//     chunk -- touches 16 distinct bank groups;
+//   - slice s is fetched into stage s % STAGES at iteration s - (STAGES - 1),
+//     behind STAGES - 1 iterations of MFMA work.  One barrier per iteration:
+//     after it every wave's share of the current slice has landed (each wave
+//     waits for its own first) and every wave has finished reading the stage
+//     the next fetch overwrites (it was read in the previous iteration).  The
+//     stages are separate LDS arrays and the waits explicit; fetches past the
+//     last slice re-read it, into stages never read again, so the number of
+//     loads in flight at each wait is the same every iteration;
+//   - gate/up tiles hold BN/2 gate rows and the BN/2 up rows of the same
+//     channels; each wave's columns are WN/2 gate + the matching WN/2 up
+//     channels, so silu(g) * u is formed in registers;
 //   - routed rows are gathered through the expert-sorted token list;
-//   - work items are (expert tile, n-tile) with n fastest; a work-group's
-//     position is mapped so that consecutive items -- the n-tiles sharing an
-//     expert's rows, and the m-tiles sharing its weights -- land on the same
-//     XCD (work-groups are spread over the 8 XCDs round-robin), so the shared
-//     operand is read from that XCD's L2.
+//   - work items are (expert tile, n-tile) with n fastest; XCD j runs the j-th
+//     eighth of the items, in order, so the n-tiles of one expert tile (which
+//     gather the same rows) and consecutive expert tiles (same weights) share
+//     that XCD's L2.
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
@@ -28,186 +42,441 @@ namespace flint {
 
 namespace {
 
-constexpr int TBM = 128, TBN = 128, TBK = 64;
-constexpr int kPitch = TBK + 8;  // bf16 elements per LDS row (144 bytes)
 constexpr int kXcds = 8;
+constexpr int kLdsBytes = 160 * 1024;
 
-// item index seen by this work-group: blockIdx.x % 8 selects the XCD; the
-// items of one XCD are consecutive.
-__device__ __forceinline__ int xcd_item(int grid)
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Tile configuration: work-group tile BM x BN, wave tile WM x WN, k slice BK
+// (32 or 64) per LDS stage, STAGES stages.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+    static constexpr int WAVES_N = BN / WN, WAVES = (BM / WM) * WAVES_N, THREADS = 64 * WAVES;
+    static constexpr int MB = WM / 16, NB = WN / 16;
+    static constexpr int CPR = BK / 8;               // 16-byte chunks per LDS row
+    static constexpr int ROWS_PER_LOAD = 64 / CPR;   // rows one load instruction covers
+    static constexpr int NQ = BK / 32;               // 32-wide MFMA steps per slice
+    static constexpr int STAGE_ELEMS = (BM + BN) * BK;
+    static constexpr int LOADS_A = BM / ROWS_PER_LOAD / WAVES, LOADS_B = BN / ROWS_PER_LOAD / WAVES;
+    static constexpr int LDS = STAGES * STAGE_ELEMS * 2;
+    static constexpr int WGS_PER_CU = kLdsBytes / LDS >= 2 ? 2 : 1;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 16 == 0 && WN % 32 == 0, "tile shape");
+    static_assert(BK == 32 || BK == 64, "slice");
+    static_assert(LOADS_A * ROWS_PER_LOAD * WAVES == BM && LOADS_B * ROWS_PER_LOAD * WAVES == BN, "rows per wave");
+    static_assert(STAGES >= 3 && STAGES <= 8 && LDS <= kLdsBytes, "stages");
+    // slices per unrolled round: stage index and fragment-buffer parity both static
+    static constexpr int ROUND = (NQ == 1 && STAGES % 2) ? 2 * STAGES : STAGES;
+    // stored chunk position of logical chunk c in row r
+    __device__ static __forceinline__ int swz(int r, int c) { return CPR == 8 ? c ^ (r & 7) : c ^ ((r >> 1) & 3); }
+};
+
+// Configurations (chosen per launch by the host).
+#ifndef FLINT_TL_ROTATE
+#define FLINT_TL_ROTATE 1
+#endif
+#ifndef FLINT_TL_S_BK
+#define FLINT_TL_S_BK 32
+#endif
+#ifndef FLINT_TL_S_ST
+#define FLINT_TL_S_ST 5
+#endif
+#ifndef FLINT_TL_B_ST
+#define FLINT_TL_B_ST 4
+#endif
+using CfgSmall = Cfg<128, 128, 64, 64, FLINT_TL_S_BK, FLINT_TL_S_ST>;  // 4 waves
+using CfgWide = Cfg<256, 128, 128, 64, 32, 6>;                         // 4 waves
+using CfgBig = Cfg<256, 256, 128, 128, 32, FLINT_TL_B_ST>;             // 4 waves
+using CfgBig8 = Cfg<256, 256, 128, 64, 32, FLINT_TL_B_ST>;             // 8 waves
+
+// Item of this work-group, or -1 (see the file comment).  Work-groups are
+// dealt to the XCDs round-robin (blockIdx.x % 8 is the XCD); the grid is sized
+// for the most items the routing can produce.
+__device__ __forceinline__ int xcd_item(int total)
 {
-    const int per = grid / kXcds;  // the launcher rounds the grid to a multiple of 8
-    return (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int item = (blockIdx.x % kXcds) * per + slot;
+    return (slot < per && item < total) ? item : -1;
 }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others at their "no wait" maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+enum Mode { GATE_UP = 0, DOWN = 1, ROUTER = 2 };
 
 }  // namespace
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256, 2) void k_tiled(ExpertArgs a, int n_shared_items)
+struct TiledArgs {
+    ExpertArgs e;
+    int n_shared;        // shared-expert items (they come first)
+    const void *router;  // ROUTER: [E][H]
+    const float *bias;   // ROUTER: [E] or null
+    float *logits;       // ROUTER: [T][E]
+};
+
+template <int MODE, typename C>
+__global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs ta)
 {
     using S = uint16_t;
-    __shared__ __attribute__((aligned(16))) S lds_a[2][TBM * kPitch];
-    __shared__ __attribute__((aligned(16))) S lds_b[2][TBN * kPitch];
+    constexpr int BM = C::BM, BN = C::BN, MB = C::MB, NB = C::NB, STAGES = C::STAGES;
+    // one LDS array per stage (separate objects, so the compiler can tell the
+    // stage being filled from the stage being read)
+    __shared__ __attribute__((aligned(16))) S st0[C::STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) S st1[C::STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) S st2[C::STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) S st3[STAGES > 3 ? C::STAGE_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) S st4[STAGES > 4 ? C::STAGE_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) S st5[STAGES > 5 ? C::STAGE_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) S st6[STAGES > 6 ? C::STAGE_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) S st7[STAGES > 7 ? C::STAGE_ELEMS : 8];
+    auto stage = [&](int i) -> S * {
+        return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : i == 3 ? st3 : i == 4 ? st4 : i == 5 ? st5 : i == 6 ? st6 : st7;
+    };
 
+    const ExpertArgs &a = ta.e;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int H = a.H;
 
-    // ---- the work item
-    const int item = xcd_item(gridDim.x);
-    const int ntn_shared = GATE_UP ? a.Is / (TBN / 2) : (H + TBN - 1) / TBN;
-    const int ntn_routed = GATE_UP ? a.I / (TBN / 2) : (H + TBN - 1) / TBN;
-    bool shared = item < n_shared_items;
+    // ---- the work item: rows [row0, row_end) of A, n-tile nt, reduction kdim
     int row0, row_end, nt, kdim, e = 0;
-    if (shared) {
-        row0 = (item / ntn_shared) * TBM;
-        nt = item % ntn_shared;
+    bool shared = false;
+    if (MODE == ROUTER) {
+        const int ntn = (a.E + BN - 1) / BN;
+        const int item = xcd_item(((a.T + BM - 1) / BM) * ntn);
+        if (item < 0) return;
+        row0 = (item / ntn) * BM;
+        nt = item % ntn;
         row_end = a.T;
-        kdim = GATE_UP ? H : a.Is;
+        kdim = H;
     } else {
-        const int r = item - n_shared_items;
-        const int entry = r / ntn_routed;
-        const int nlist = GATE_UP ? a.meta[0] : a.meta[1];
-        if (entry >= nlist) return;  // (the grid is rounded up past the list's capacity)
-        const int32_t *list = GATE_UP ? a.list1 : a.list2;
-        e = list[2 * entry];
-        row0 = list[2 * entry + 1];
-        nt = r % ntn_routed;
-        row_end = a.offsets[e + 1];
-        kdim = GATE_UP ? H : a.I;
+        const int ntn_shared = MODE == GATE_UP ? a.Is / (BN / 2) : (H + BN - 1) / BN;
+        const int ntn_routed = MODE == GATE_UP ? a.I / (BN / 2) : (H + BN - 1) / BN;
+        const int nlist = MODE == GATE_UP ? a.meta[0] : a.meta[1];
+        const int item = xcd_item(ta.n_shared + nlist * ntn_routed);
+        if (item < 0) return;
+        shared = item < ta.n_shared;
+        if (shared) {
+            row0 = (item / ntn_shared) * BM;
+            nt = item % ntn_shared;
+            row_end = a.T;
+            kdim = MODE == GATE_UP ? H : a.Is;
+        } else {
+            const int r = item - ta.n_shared;
+            const int entry = r / ntn_routed;
+            const int32_t *list = MODE == GATE_UP ? a.list1 : a.list2;
+            e = list[2 * entry];
+            row0 = list[2 * entry + 1];
+            nt = r % ntn_routed;
+            row_end = a.offsets[e + 1];
+            kdim = MODE == GATE_UP ? H : a.I;
+        }
     }
 
-    // ---- global source rows of the 4 A chunks and 4 B chunks this thread copies
-    // chunk c = tid + 256*i: row c/8 (0..127), 16-byte column (c%8)
-    const int ccol = (tid & 7) * 8;  // element offset within the 64-wide slice
-    const S *ga[4];
-    const S *gb[4];
+    // ---- this lane's fetch sources.  Load instruction i of this wave covers
+    // ROWS_PER_LOAD rows of A (or of B); the lane takes row + lane / CPR and
+    // the logical chunk whose stored position is lane % CPR.
+    constexpr int BK = C::BK, CPR = C::CPR, RPL = C::ROWS_PER_LOAD;
+    const S *ga[C::LOADS_A];
+    const S *gb[C::LOADS_B];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = (tid >> 3) + 32 * i;  // tile row
+    for (int i = 0; i < C::LOADS_A; ++i) {
+        const int rr = (wave * C::LOADS_A + i) * RPL + lane / CPR;
+        const int chunk = C::swz(rr, lane % CPR) * 8;  // (the swizzle is its own inverse)
         int r = row0 + rr;
         if (r >= row_end) r = row0;  // padded rows repeat the first row
-        if (GATE_UP) {
+        if (MODE == GATE_UP) {
             const int tok = shared ? r : a.sorted_token[r];
-            ga[i] = (const S *)a.x + (size_t)tok * H + ccol;
+            ga[i] = (const S *)a.x + (size_t)tok * H + chunk;
+        } else if (MODE == DOWN) {
+            ga[i] = (shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * kdim + chunk;
         } else {
-            ga[i] = (shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * kdim + ccol;
+            ga[i] = (const S *)a.x + (size_t)r * H + chunk;
         }
-        if (GATE_UP) {
-            // B rows 0..63: gate channels nt*64 + rr; rows 64..127: the same up channels
-            const int ch = nt * 64 + (rr & 63);
-            const S *w = shared ? (rr < 64 ? (const S *)a.shared_gate : (const S *)a.shared_up)
-                                : (rr < 64 ? (const S *)a.gate : (const S *)a.up) + (size_t)e * a.I * H;
-            gb[i] = w + (size_t)ch * H + ccol;
-        } else {
-            int c = nt * TBN + rr;
+    }
+#pragma unroll
+    for (int i = 0; i < C::LOADS_B; ++i) {
+        const int rr = (wave * C::LOADS_B + i) * RPL + lane / CPR;
+        const int chunk = C::swz(rr, lane % CPR) * 8;
+        if (MODE == GATE_UP) {
+            // B rows [0, BN/2): gate channels nt*BN/2 + rr; then the same up channels
+            const int ch = nt * (BN / 2) + (rr % (BN / 2));
+            const bool up = rr >= BN / 2;
+            const S *w = shared ? (up ? (const S *)a.shared_up : (const S *)a.shared_gate)
+                                : (up ? (const S *)a.up : (const S *)a.gate) + (size_t)e * a.I * H;
+            gb[i] = w + (size_t)ch * H + chunk;
+        } else if (MODE == DOWN) {
+            int c = nt * BN + rr;
             if (c >= H) c = 0;
             const S *w = shared ? (const S *)a.shared_down : (const S *)a.down + (size_t)e * H * a.I;
-            gb[i] = w + (size_t)c * kdim + ccol;
+            gb[i] = w + (size_t)c * kdim + chunk;
+        } else {
+            int c = nt * BN + rr;
+            if (c >= a.E) c = 0;
+            gb[i] = (const S *)ta.router + (size_t)c * H + chunk;
         }
     }
-
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int k0) {
+    auto fetch = [&](S *buf, int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = *reinterpret_cast<const u32x4 *>(ga[i] + k0);
-            rb[i] = *reinterpret_cast<const u32x4 *>(gb[i] + k0);
-        }
+        for (int i = 0; i < C::LOADS_A; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(ga[i] + k0),
+                                             LDS_PTR(buf + (wave * C::LOADS_A + i) * RPL * BK), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < C::LOADS_B; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(gb[i] + k0),
+                                             LDS_PTR(buf + (BM + (wave * C::LOADS_B + i) * RPL) * BK), 16, 0, 0);
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = (tid >> 3) + 32 * i;
-            *reinterpret_cast<u32x4 *>(&lds_a[buf][rr * kPitch + ccol]) = ra[i];
-            *reinterpret_cast<u32x4 *>(&lds_b[buf][rr * kPitch + ccol]) = rb[i];
-        }
-    };
+    constexpr int kLoadsPerSlice = C::LOADS_A + C::LOADS_B;
 
-    // ---- wave fragments: 4 row blocks (A) x 4 column blocks (B) of 16
-    // A rows: wm*64 + m*16 + (lane&15).  B rows (GATE_UP): gate blocks j<2 at
-    // wn*32 + j*16, up blocks j>=2 at 64 + wn*32 + (j-2)*16; (down) wn*64 + j*16.
-    int boff[4], aoff[4];
-    const int kq = (lane >> 4) * 8;
+    // ---- fragments: MB row blocks (A) x NB column blocks (B) of 16.
+    // A rows: wm*WM + m*16 + (lane&15).  B rows (GATE_UP): gate blocks j < NB/2
+    // at wn*WN/2 + j*16, up blocks at BN/2 + wn*WN/2 + (j - NB/2)*16;
+    // otherwise wn*WN + j*16.  Every fragment row is congruent to lane & 15
+    // mod 16, so its swizzle depends on the lane only.
+    int aoff[MB], boff[NB];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) aoff[m] = (wm * 64 + m * 16 + (lane & 15)) * kPitch + kq;
+    for (int m = 0; m < MB; ++m) aoff[m] = (wm * C::WM + m * 16 + (lane & 15)) * BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int br = GATE_UP ? (j < 2 ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16) : wn * 64 + j * 16;
-        boff[j] = (br + (lane & 15)) * kPitch + kq;
+    for (int j = 0; j < NB; ++j) {
+        const int br = MODE == GATE_UP ? (j < NB / 2 ? wn * (C::WN / 2) + j * 16
+                                                     : BN / 2 + wn * (C::WN / 2) + (j - NB / 2) * 16)
+                                       : wn * C::WN + j * 16;
+        boff[j] = (BM + br + (lane & 15)) * BK;
     }
+    int qoff[C::NQ];  // element offset of this lane's 8 k values in 32-wide step q
+#pragma unroll
+    for (int q = 0; q < C::NQ; ++q) qoff[q] = C::swz(lane & 15, q * 4 + (lane >> 4)) * 8;
 
-    f32x4 acc[4][4];
+    struct Frags {
+        Frag<BF16> a[MB], b[NB];
+    };
+    auto read = [&](Frags &f, const S *buf, int q) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) f.a[m].load(buf + aoff[m] + qoff[q]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) f.b[j].load(buf + boff[j] + qoff[q]);
+    };
+    f32x4 acc[MB][NB];
+    auto mmas = [&](const Frags &f) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) mma(acc[m][j], f.a[m], f.b[j]);
+    };
+    // the next step's fragment reads spread over this step's MFMAs
+    constexpr int kReads = MB + NB, kMfma = MB * NB, kPer = kMfma / kReads;
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < kReads; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);  // kPer MFMAs
+        }
+        if (kMfma > kPer * kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPer * kReads, 0);
+    };
+
+    // ---- main loop.  Step (kt, q) runs the MFMAs of 32-wide step q of slice
+    // kt (in stage kt % STAGES) from fragment buffer p while the reads of the
+    // next step go to the other buffer.  At the last step of a slice: wait
+    // until this lane's part of slice kt+1 has landed, barrier (now all of it
+    // has, and every wave is done with the stage of slice kt-1), refill that
+    // stage with slice kt+STAGES-1, and read the first step of slice kt+1.
     zero_acc(acc);
-    const int nk = kdim / TBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * TBK);
-#pragma unroll
-        for (int kk = 0; kk < TBK; kk += 32) {
-            Frag<BF16> fa[4], fb[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) fa[m].load(&lds_a[buf][aoff[m] + kk]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j].load(&lds_b[buf][boff[j] + kk]);
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) mma(acc[m][j], fa[m], fb[j]);
+    const int nk = kdim / BK;
+    // Down products: each work-group walks k from its own starting slice, so
+    // that the work-groups running at once read different columns of their
+    // 1 KB rows (measured faster).  Gate/up products keep one order: there the
+    // n-tiles of an expert tile read the same gathered rows at the same time,
+    // from L2.
+    const int rot = (MODE == DOWN && FLINT_TL_ROTATE) ? (int)(blockIdx.x * 7u % (unsigned)nk) : 0;
+    auto kofs = [&](int s) {
+        s = min(s, nk - 1) + rot;
+        return (s >= nk ? s - nk : s) * BK;
+    };
+    Frags fr[2];
+    // j: position in the unrolled round (stage j % STAGES)
+    auto step = [&](int j, int q, int kt) {
+        const int p = (j * C::NQ + q) & 1;
+        const int st = j % STAGES;
+        wait_lds();  // fr[p] has landed
+        __builtin_amdgcn_sched_barrier(0);
+        if (q == C::NQ - 1) {
+            wait_vmcnt<(STAGES - 3) * kLoadsPerSlice>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(stage((st + STAGES - 1) % STAGES), kofs(kt + STAGES - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            read(fr[p ^ 1], stage((st + 1) % STAGES), 0);
+        } else {
+            read(fr[p ^ 1], stage(st), q + 1);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue
+        mmas(fr[p]);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int s = 0; s + 1 < STAGES; ++s) fetch(stage(s), kofs(s));
+    wait_vmcnt<(STAGES - 2) * kLoadsPerSlice>();
+    __builtin_amdgcn_s_barrier();
+    read(fr[0], stage(0), 0);
+    // whole rounds, with no branch inside (so the compiler keeps its own waits
+    // off the LDS reads); then the rest
+    constexpr int ROUND = C::ROUND;
+    const int nfull = nk / ROUND * ROUND;
+    for (int kb = 0; kb < nfull; kb += ROUND) {
+#pragma unroll
+        for (int j = 0; j < ROUND; ++j)
+#pragma unroll
+            for (int q = 0; q < C::NQ; ++q) step(j, q, kb + j);
+    }
+#pragma unroll
+    for (int j = 0; j + 1 < ROUND; ++j) {
+        if (nfull + j >= nk) break;
+#pragma unroll
+        for (int q = 0; q < C::NQ; ++q) step(j, q, nfull + j);
+    }
+    // no load may still be writing this work-group's LDS when it exits
+    wait_vmcnt<0>();
+    wait_lds();
+
+    // ---- epilogue: lane holds C[(lane>>4)*4 + i][lane&15] of each 16x16 block
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = row0 + wm * 64 + m * 16 + (lane >> 4) * 4 + i;
-            if (r >= row_end || r >= row0 + TBM) continue;
-            if (GATE_UP) {
+            const int rl = wm * C::WM + m * 16 + (lane >> 4) * 4 + i;
+            const int r = row0 + rl;
+            if (r >= row_end) continue;
+            if (MODE == GATE_UP) {
                 S *hout = shared ? (S *)a.h_shared : (S *)a.h_sorted;
                 const int width = shared ? a.Is : a.I;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int ch = nt * 64 + wn * 32 + j * 16 + (lane & 15);
-                    hout[(size_t)r * width + ch] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + 2][i]));
+                for (int j = 0; j < NB / 2; ++j) {
+                    const int ch = nt * (BN / 2) + wn * (C::WN / 2) + j * 16 + (lane & 15);
+                    hout[(size_t)r * width + ch] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + NB / 2][i]));
                 }
-            } else {
+            } else if (MODE == DOWN) {
                 float *yout = shared ? a.y_shared : a.y_sorted;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = nt * TBN + wn * 64 + j * 16 + (lane & 15);
+                for (int j = 0; j < NB; ++j) {
+                    const int c = nt * BN + wn * C::WN + j * 16 + (lane & 15);
                     if (c < H) yout[(size_t)r * H + c] = acc[m][j][i];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int c = nt * BN + wn * C::WN + j * 16 + (lane & 15);
+                    if (c < a.E) ta.logits[(size_t)r * a.E + c] = acc[m][j][i] + (ta.bias ? ta.bias[c] : 0.f);
                 }
             }
         }
     }
 }
 
-bool tiled_eligible(int H, int I, int Is, bool bf16)
+// ---------------------------------------------------------------------------
+// Host side
+
+#ifndef FLINT_TL_BIG_ROWS
+#define FLINT_TL_BIG_ROWS 256  // mean rows per expert from which the big configurations are used
+#endif
+#ifndef FLINT_TL_GU_SMALL
+#define FLINT_TL_GU_SMALL 0  // gate/up below that: 0 CfgSmall, 1 CfgWide
+#endif
+#ifndef FLINT_TL_GU_BIG
+#define FLINT_TL_GU_BIG 2  // gate/up from there: 2 CfgBig, 3 CfgBig8 (or 0, 1)
+#endif
+#ifndef FLINT_TL_DN_SMALL
+#define FLINT_TL_DN_SMALL 0
+#endif
+#ifndef FLINT_TL_DN_BIG
+#define FLINT_TL_DN_BIG 2
+#endif
+#ifndef FLINT_TL_ROUTER
+#define FLINT_TL_ROUTER 0
+#endif
+
+namespace {
+
+int cfg_bm(int which) { return which >= 1 ? 256 : 128; }
+int cfg_bn(int which) { return which >= 2 ? 256 : 128; }
+
+bool big_batch(int T, int K, int E) { return (long long)T * K >= (long long)FLINT_TL_BIG_ROWS * E; }
+int gu_cfg(int T, int K, int E) { return big_batch(T, K, E) ? FLINT_TL_GU_BIG : FLINT_TL_GU_SMALL; }
+int dn_cfg(int T, int K, int E) { return big_batch(T, K, E) ? FLINT_TL_DN_BIG : FLINT_TL_DN_SMALL; }
+
+template <int MODE, typename C>
+hipError_t launch_cfg(TiledArgs ta, hipStream_t stream, Marks m)
 {
-    // k slices of 64; gate/up tiles of 64 channels
-    return bf16 && H % TBK == 0 && I % 64 == 0 && Is % 64 == 0;
+    const ExpertArgs &a = ta.e;
+    const int mt = (a.T + C::BM - 1) / C::BM;
+    int items;
+    if (MODE == ROUTER) {
+        items = mt * ((a.E + C::BN - 1) / C::BN);
+    } else {
+        const int ntn_s = MODE == GATE_UP ? a.Is / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
+        const int ntn_r = MODE == GATE_UP ? a.I / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
+        ta.n_shared = a.Is > 0 ? mt * ntn_s : 0;
+        items = ta.n_shared + list_capacity(a.T, a.K, a.E, C::BM) * ntn_r;
+    }
+    const int grid = (items + kXcds - 1) / kXcds * kXcds;
+    return launch_k(k_tiled<MODE, C>, grid, C::THREADS, 0, stream, m, ta);
 }
+
+template <int MODE>
+hipError_t launch_mode(int which, const TiledArgs &ta, hipStream_t stream, Marks m)
+{
+    switch (which) {
+    case 1: return launch_cfg<MODE, CfgWide>(ta, stream, m);
+    case 2: return launch_cfg<MODE, CfgBig>(ta, stream, m);
+    case 3: return launch_cfg<MODE, CfgBig8>(ta, stream, m);
+    default: return launch_cfg<MODE, CfgSmall>(ta, stream, m);
+    }
+}
+
+}  // namespace
+
+bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16)
+{
+    // whole k slices (H, I, Is); a gate/up tile takes BN/2 gate channels and
+    // the same up channels
+    const int half = cfg_bn(gu_cfg(T, K, E)) / 2;
+    return bf16 && H % 64 == 0 && I % 64 == 0 && Is % 64 == 0 && I % half == 0 && Is % half == 0;
+}
+
+int tiled_bm1(int T, int K, int E) { return cfg_bm(gu_cfg(T, K, E)); }
+int tiled_bm2(int T, int K, int E) { return cfg_bm(dn_cfg(T, K, E)); }
 
 hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
-    const int cap1 = list_capacity(a.T, a.K, a.E, TBM);
-    const int cap2 = cap1;
-    const int mt = (a.T + TBM - 1) / TBM;
-    const int ns1 = a.Is > 0 ? mt * (a.Is / (TBN / 2)) : 0;
-    const int ns2 = a.Is > 0 ? mt * ((a.H + TBN - 1) / TBN) : 0;
-    auto round8 = [](int g) { return (g + kXcds - 1) / kXcds * kXcds; };
-    const int g1 = round8(ns1 + cap1 * (a.I / (TBN / 2)));
-    const int g2 = round8(ns2 + cap2 * ((a.H + TBN - 1) / TBN));
-    const hipError_t err = launch_k(k_tiled<true>, g1, 256, 0, stream, marks ? marks[0] : Marks{}, a, ns1);
+    TiledArgs ta{};
+    ta.e = a;
+    const hipError_t err = launch_mode<GATE_UP>(gu_cfg(a.T, a.K, a.E), ta, stream, marks ? marks[0] : Marks{});
     if (err != hipSuccess) return err;
-    return launch_k(k_tiled<false>, g2, 256, 0, stream, marks ? marks[1] : Marks{}, a, ns2);
+    return launch_mode<DOWN>(dn_cfg(a.T, a.K, a.E), ta, stream, marks ? marks[1] : Marks{});
+}
+
+bool tiled_router_eligible(int T, int H, bool bf16) { return bf16 && T >= 1024 && H % 64 == 0; }
+
+hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
+                               float *logits, hipStream_t stream, Marks m)
+{
+    TiledArgs ta{};
+    ta.e.x = x;
+    ta.e.T = T;
+    ta.e.H = H;
+    ta.e.E = E;
+    ta.router = router;
+    ta.bias = bias;
+    ta.logits = logits;
+    return launch_mode<ROUTER>(FLINT_TL_ROUTER, ta, stream, m);
 }
 
 }  // namespace flint
