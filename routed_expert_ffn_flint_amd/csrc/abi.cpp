@@ -86,7 +86,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
         off += align_up(bytes ? bytes : 1);
         return p;
     };
-    w.logits = (float *)take((size_t)T * E * 4);
+    w.logits = (float *)take((size_t)router_splits(T, H, eb == 2) * T * E * 4);
     w.hist = (int32_t *)take((size_t)ntiles * E * 4);
     w.tile_base = (int32_t *)take((size_t)ntiles * E * 4);
     w.rank = (int32_t *)take(TK * 4);
@@ -164,6 +164,7 @@ flint_status flint_moe_route(const flint_moe_dims *d, int32_t T, const void *x, 
     a.E = d->n_experts;
     a.K = d->top_k;
     a.logits = w.logits;
+    a.logit_splits = router_splits(T, d->hidden, d->dtype == FLINT_BF16);
     a.topk_idx = topk_idx;
     a.topk_w = topk_w;
     a.compute_topk = true;
@@ -273,6 +274,7 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
 
     DispatchArgs a = dispatch_args(d, T, w);
     a.logits = w.logits;
+    a.logit_splits = router_splits(T, d->hidden, bf16);
     a.topk_idx = topk_idx_out ? topk_idx_out : w.topk_idx;
     a.topk_w = topk_w_out ? topk_w_out : w.topk_w;
     a.compute_topk = true;
@@ -311,7 +313,7 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     e.out = out;
     e.out_bf16 = out_dtype == FLINT_BF16;
     e.tiles = tiles;
-    e.grid_cap = stream_wgs_per_cu() * device_cus();
+    e.cus = device_cus();
     if (launch_experts(e, s, events ? marks + 2 : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
     return FLINT_OK;
 }

@@ -309,7 +309,7 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
     const dim3 gc(a.T, (a.H + 1023) / 1024);
     if (t.stream || t.tiled) {
         const hipError_t err =
-            t.stream ? launch_experts_stream(a, a.grid_cap, stream, marks) : launch_experts_tiled(a, stream, marks);
+            t.stream ? launch_experts_stream(a, stream, marks) : launch_experts_tiled(a, stream, marks);
         if (err != hipSuccess) return err;
         return launch_k(k_combine, gc, 256, 0, stream, m3, a);
     }

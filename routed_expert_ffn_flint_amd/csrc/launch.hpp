@@ -64,7 +64,7 @@ ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf1
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
-    float *logits;        // [T][E]
+    float *logits;        // [splits][T][E] (partial sums over slices of H; see router_splits)
     int32_t *hist;        // [ntiles][E]
     int32_t *tile_base;   // [ntiles][E]
     int32_t *rank;        // [T*K]
@@ -91,14 +91,20 @@ int list_capacity(int T, int K, int E, int bm);
 
 // ---- launches (all enqueue on `stream`, return hipGetLastError()) ----------
 
-// logits[t][e] = x[t] . router[e] (+ bias[e]), float32.
+// Number of partial logit arrays the router writes (the sum over slices of H
+// is split for large batches); the top-k kernels add them in order.
+int router_splits(int T, int H, bool bf16);
+
+// logits[t][e] = x[t] . router[e] (+ bias[e]), float32, as router_splits
+// partial arrays (bias in the first) that sum to it.
 hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const void *router,
                                 const float *bias, int E, float *logits, hipStream_t stream, Marks m = {});
 
 // Top-k selection and/or dispatch.  See route.hip for the modes.
 struct DispatchArgs {
     int T, E, K;
-    const float *logits;      // when compute_topk
+    const float *logits;      // when compute_topk: logit_splits arrays of [T][E] to add
+    int logit_splits;
     int32_t *topk_idx;        // out when compute_topk, in otherwise
     float *topk_w;            // out when compute_topk
     bool compute_topk;
@@ -124,19 +130,18 @@ struct ExpertArgs {
     void *out;
     bool out_bf16;
     ExpertTiles tiles;
-    int grid_cap;  // work-groups for the persistent kernels (from the device's CU count)
+    int cus;  // compute units of the device (sizes the persistent kernels' grids)
 };
 // marks (nullable): 3 stages, gate/up (+ shared), down (+ shared), combine.
 hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 
 // Persistent streaming kernels (small batches, shapes whose H, I, Is split into
-// whole batches); grid_cap: work-groups to launch at most (a few per CU).
+// whole batches), a few work-groups per CU.
 bool stream_eligible(int T, int H, int I, int Is);
 int stream_bm1();
 int stream_bm2();
-int stream_wgs_per_cu();
 // marks (nullable): gate/up and down stages.
-hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, const Marks *marks);
+hipError_t launch_experts_stream(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 
 // LDS-tiled kernels for large bf16 batches: rows per gate/up and per down tile
 // (128 or 256, from the mean rows per expert), eligibility, launch.
@@ -146,6 +151,7 @@ bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16);
 hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 // The router product on the same tiles (large bf16 batches).
 bool tiled_router_eligible(int T, int H, bool bf16);
+constexpr int kRouterSplits = 4;
 hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
                                float *logits, hipStream_t stream, Marks m);
 

@@ -203,7 +203,8 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off)
 // and the other reversed (a bitonic sequence), which a 3-stage bitonic network
 // sorts.  Every lane of the group ends with the same list.
 template <int G>
-__device__ __forceinline__ void group_top8(const float *zt, int E, uint64_t (&l)[kMaxTopK])
+__device__ __forceinline__ void group_top8(const float *zt, size_t split_stride, int nsplit, int E,
+                                           uint64_t (&l)[kMaxTopK])
 {
     constexpr int C = kMaxExperts / G;
     const int gl = threadIdx.x & (G - 1);
@@ -212,7 +213,12 @@ __device__ __forceinline__ void group_top8(const float *zt, int E, uint64_t (&l)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int e = gl + G * i;
-        uint64_t k = e < E ? sel_key(score_from_logit(zt[e]), e) : 0;
+        float z = 0.f;
+        if (e < E) {
+            z = zt[e];
+            for (int sp = 1; sp < nsplit; ++sp) z += zt[sp * split_stride + e];  // partial sums, in order
+        }
+        uint64_t k = e < E ? sel_key(score_from_logit(z), e) : 0;
         if (C <= kMaxTopK) {
             l[i] = k;  // fewer candidates than list slots: keep all, sort below
         } else if (k > l[kMaxTopK - 1]) {
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(256) void k_topk(DispatchArgs da)
     const int gl = threadIdx.x & (G - 1);
     const int t = tok < T ? tok : T - 1;  // whole groups share a token; extra groups redo the last one
     uint64_t l[kMaxTopK];
-    group_top8<G>(logits + (size_t)t * E, E, l);
+    group_top8<G>(logits + (size_t)t * E, (size_t)T * E, da.logit_splits, E, l);
     if (tok < T) write_topk(l, t, K, gl, topk_idx, topk_w);
 }
 

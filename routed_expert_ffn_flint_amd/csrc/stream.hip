@@ -38,10 +38,16 @@
 #ifndef FLINT_ST_MB1
 #define FLINT_ST_MB1 2  // gate/up items: MB1 blocks of 16 rows
 #endif
-#ifndef FLINT_ST_WGS
-#define FLINT_ST_WGS 2  // resident work-groups per CU (register and LDS budget)
+#ifndef FLINT_ST_WGS1
+#define FLINT_ST_WGS1 2  // gate/up: work-groups per CU (the grid; also the occupancy asked for)
+#endif
+#ifndef FLINT_ST_WGS2
+#define FLINT_ST_WGS2 2  // down
 #endif
 
+#ifndef FLINT_ST_MAXT
+#define FLINT_ST_MAXT 512  // largest batch served by these kernels
+#endif
 #ifndef FLINT_ST_MB2
 #define FLINT_ST_MB2 2  // down items: MB2 blocks of 16 rows
 #endif
@@ -52,27 +58,21 @@ namespace {
 
 constexpr int kWaves = 4;
 
-// Dispatch tables in LDS: list (expert, first slot) pairs, offsets[E+1],
-// sorted_token[T*K] (gate/up only).
+// Dispatch tables in LDS: list (expert, first slot) pairs, offsets[E+1].
 struct Tables {
     int32_t *list;
     int32_t *offsets;
-    int32_t *sorted_token;
     int nlist;
 };
 
-__device__ __forceinline__ Tables load_tables(const ExpertArgs &a, const int32_t *glist, int nlist, bool with_tokens,
-                                              int32_t *lds)
+__device__ __forceinline__ Tables load_tables(const ExpertArgs &a, const int32_t *glist, int nlist, int32_t *lds)
 {
     Tables t;
     t.nlist = nlist;
     t.list = lds;
     t.offsets = lds + 2 * nlist;
-    t.sorted_token = t.offsets + (a.E + 1);
     for (int i = threadIdx.x; i < 2 * nlist; i += blockDim.x) t.list[i] = glist[i];
     for (int i = threadIdx.x; i <= a.E; i += blockDim.x) t.offsets[i] = a.offsets[i];
-    if (with_tokens)
-        for (int i = threadIdx.x; i < a.T * a.K; i += blockDim.x) t.sorted_token[i] = a.sorted_token[i];
     __syncthreads();
     return t;
 }
@@ -93,7 +93,8 @@ struct Item {
 
 // GATE_UP: gate/up + SwiGLU -> h (dtype);  otherwise: down -> y (float32).
 template <typename DT, int MB, int NB, int U, bool GATE_UP>
-__global__ __launch_bounds__(256, FLINT_ST_WGS) void k_expert_stream(ExpertArgs a, int n_shared_items)
+__global__ __launch_bounds__(256, GATE_UP ? FLINT_ST_WGS1 : FLINT_ST_WGS2) void k_expert_stream(ExpertArgs a,
+                                                                                          int n_shared_items)
 {
     using S = typename DT::storage;
     constexpr int BM = MB * 16;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256, FLINT_ST_WGS) void k_expert_stream(ExpertArgs 
     const int kg = (lane >> 4) * 8;
     const int H = a.H;
     const int nlist = GATE_UP ? a.meta[0] : a.meta[1];
-    const Tables tab = load_tables(a, GATE_UP ? a.list1 : a.list2, nlist, GATE_UP, dyn_lds);
+    const Tables tab = load_tables(a, GATE_UP ? a.list1 : a.list2, nlist, dyn_lds);
 
     const int ntn_shared = GATE_UP ? a.Is / BN : (H + BN - 1) / BN;
     const int ntn_routed = GATE_UP ? a.I / BN : (H + BN - 1) / BN;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256, FLINT_ST_WGS) void k_expert_stream(ExpertArgs 
             int r = it.row0 + m * 16 + (lane & 15);
             if (r >= it.row_end) r = it.row0;  // rows past the tile repeat its first row (cache hits)
             if (GATE_UP) {
-                const int tok = it.shared ? r : tab.sorted_token[r];
+                const int tok = it.shared ? r : a.sorted_token[r];
                 it.a[m] = (const S *)a.x + (size_t)tok * H + kg;
             } else {
                 it.a[m] = (it.shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * it.kdim + kg;
@@ -282,11 +283,10 @@ static int unroll_down(int I, int Is)
 
 bool stream_eligible(int T, int H, int I, int Is)
 {
-    return T <= kStreamMaxT && unroll_gate_up(H) > 0 && unroll_down(I, Is) > 0;
+    return T <= FLINT_ST_MAXT && unroll_gate_up(H) > 0 && unroll_down(I, Is) > 0;
 }
 int stream_bm1() { return FLINT_ST_MB1 * 16; }
 int stream_bm2() { return FLINT_ST_MB2 * 16; }
-int stream_wgs_per_cu() { return FLINT_ST_WGS; }
 
 template <typename DT, int U, bool GATE_UP>
 static hipError_t launch_one(const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream, Marks m)
@@ -307,7 +307,7 @@ static hipError_t launch_u(int U, const ExpertArgs &a, int grid, int n_shared, s
 }
 
 template <typename DT>
-static hipError_t launch_stream_t(const ExpertArgs &a, int grid_cap, hipStream_t stream, const Marks *marks)
+static hipError_t launch_stream_t(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
     const int bm1 = FLINT_ST_MB1 * 16, bm2 = FLINT_ST_MB2 * 16;
     const int bn1 = FLINT_ST_NB1 / 2 * 16, bn2 = FLINT_ST_NB2 * 16;
@@ -317,18 +317,18 @@ static hipError_t launch_stream_t(const ExpertArgs &a, int grid_cap, hipStream_t
     const int ns2 = a.Is > 0 ? (a.T + bm2 - 1) / bm2 * ((a.H + bn2 - 1) / bn2) : 0;
     const int max1 = ns1 + cap1 * (a.I / bn1);
     const int max2 = ns2 + cap2 * ((a.H + bn2 - 1) / bn2);
-    const size_t lds1 = (size_t)(2 * cap1 + a.E + 1 + a.T * a.K) * 4;
+    const size_t lds1 = (size_t)(2 * cap1 + a.E + 1) * 4;
     const size_t lds2 = (size_t)(2 * cap2 + a.E + 1) * 4;
-    const hipError_t err = launch_u<DT, true>(unroll_gate_up(a.H), a, min(grid_cap, max1), ns1, lds1, stream,
+    const hipError_t err = launch_u<DT, true>(unroll_gate_up(a.H), a, min(FLINT_ST_WGS1 * a.cus, max1), ns1, lds1, stream,
                                               marks ? marks[0] : Marks{});
     if (err != hipSuccess) return err;
-    return launch_u<DT, false>(unroll_down(a.I, a.Is), a, min(grid_cap, max2), ns2, lds2, stream,
+    return launch_u<DT, false>(unroll_down(a.I, a.Is), a, min(FLINT_ST_WGS2 * a.cus, max2), ns2, lds2, stream,
                                marks ? marks[1] : Marks{});
 }
 
-hipError_t launch_experts_stream(const ExpertArgs &a, int grid_cap, hipStream_t stream, const Marks *marks)
+hipError_t launch_experts_stream(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
-    return a.bf16 ? launch_stream_t<BF16>(a, grid_cap, stream, marks) : launch_stream_t<F32>(a, grid_cap, stream, marks);
+    return a.bf16 ? launch_stream_t<BF16>(a, stream, marks) : launch_stream_t<F32>(a, stream, marks);
 }
 
 }  // namespace flint

@@ -118,6 +118,7 @@ enum Mode { GATE_UP = 0, DOWN = 1, ROUTER = 2 };
 struct TiledArgs {
     ExpertArgs e;
     int n_shared;        // shared-expert items (they come first)
+    int ksplit;          // ROUTER: partial sums over this many slices of H
     const void *router;  // ROUTER: [E][H]
     const float *bias;   // ROUTER: [E] or null
     float *logits;       // ROUTER: [T][E]
@@ -150,14 +151,20 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
     // ---- the work item: rows [row0, row_end) of A, n-tile nt, reduction kdim
     int row0, row_end, nt, kdim, e = 0;
     bool shared = false;
+    int kbase = 0;  // ROUTER: first k of this split
+    float *lout = nullptr;
     if (MODE == ROUTER) {
         const int ntn = (a.E + BN - 1) / BN;
-        const int item = xcd_item(((a.T + BM - 1) / BM) * ntn);
+        const int item = xcd_item(((a.T + BM - 1) / BM) * ntn * ta.ksplit);
         if (item < 0) return;
-        row0 = (item / ntn) * BM;
-        nt = item % ntn;
+        const int ks = item % ta.ksplit, tile = item / ta.ksplit;
+        row0 = (tile / ntn) * BM;
+        nt = tile % ntn;
         row_end = a.T;
-        kdim = H;
+        kdim = H / ta.ksplit;
+        kbase = ks * kdim;
+        lout = ta.logits + (size_t)ks * a.T * a.E;
+        if (ks != 0) ta.bias = nullptr;
     } else {
         const int ntn_shared = MODE == GATE_UP ? a.Is / (BN / 2) : (H + BN - 1) / BN;
         const int ntn_routed = MODE == GATE_UP ? a.I / (BN / 2) : (H + BN - 1) / BN;
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
         } else if (MODE == DOWN) {
             ga[i] = (shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * kdim + chunk;
         } else {
-            ga[i] = (const S *)a.x + (size_t)r * H + chunk;
+            ga[i] = (const S *)a.x + (size_t)r * H + kbase + chunk;
         }
     }
 #pragma unroll
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
         } else {
             int c = nt * BN + rr;
             if (c >= a.E) c = 0;
-            gb[i] = (const S *)ta.router + (size_t)c * H + chunk;
+            gb[i] = (const S *)ta.router + (size_t)c * H + kbase + chunk;
         }
     }
     auto fetch = [&](S *buf, int k0) {
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int c = nt * BN + wn * C::WN + j * 16 + (lane & 15);
-                    if (c < a.E) ta.logits[(size_t)r * a.E + c] = acc[m][j][i] + (ta.bias ? ta.bias[c] : 0.f);
+                    if (c < a.E) lout[(size_t)r * a.E + c] = acc[m][j][i] + (ta.bias ? ta.bias[c] : 0.f);
                 }
             }
         }
@@ -419,7 +426,7 @@ hipError_t launch_cfg(TiledArgs ta, hipStream_t stream, Marks m)
     const int mt = (a.T + C::BM - 1) / C::BM;
     int items;
     if (MODE == ROUTER) {
-        items = mt * ((a.E + C::BN - 1) / C::BN);
+        items = mt * ((a.E + C::BN - 1) / C::BN) * ta.ksplit;
     } else {
         const int ntn_s = MODE == GATE_UP ? a.Is / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
         const int ntn_r = MODE == GATE_UP ? a.I / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
@@ -463,7 +470,12 @@ hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const M
     return launch_mode<DOWN>(dn_cfg(a.T, a.K, a.E), ta, stream, marks ? marks[1] : Marks{});
 }
 
-bool tiled_router_eligible(int T, int H, bool bf16) { return bf16 && T >= 1024 && H % 64 == 0; }
+bool tiled_router_eligible(int T, int H, bool bf16) { return bf16 && T >= 1024 && H % (64 * kRouterSplits) == 0; }
+
+// Split the sum over H while the batch alone gives too few tiles to fill the
+// chip (measured: faster up to 4096 tokens; at 16384 the extra partial
+// arrays cost more than they save).
+int router_splits(int T, int H, bool bf16) { return tiled_router_eligible(T, H, bf16) && T <= 4096 ? kRouterSplits : 1; }
 
 hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
                                float *logits, hipStream_t stream, Marks m)
@@ -476,6 +488,7 @@ hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, 
     ta.router = router;
     ta.bias = bias;
     ta.logits = logits;
+    ta.ksplit = router_splits(T, H, true);
     return launch_mode<ROUTER>(FLINT_TL_ROUTER, ta, stream, m);
 }
 

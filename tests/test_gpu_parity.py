@@ -50,6 +50,8 @@ SMALL = [
     ("t300",      300, 256, 64, 6, 128, 128, True, False),   # two dispatch tiles
     ("t600_f32",  600, 128, 16, 2, 64, 64,  False, False),
     ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
+    ("t2100_big", 2100, 256, 16, 4, 128, 128, True, True),   # 256-row tiles, router split over H
+    ("t5000_ns",  5000, 128, 8,  2, 128, 0,   True, False),  # 256-row tiles, no shared expert
 ]
 
 
