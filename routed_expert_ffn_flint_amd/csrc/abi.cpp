@@ -45,6 +45,10 @@ flint_status check_T(const flint_moe_dims *d, int32_t T)
 
 int elem_bytes(const flint_moe_dims *d) { return d->dtype == FLINT_BF16 ? 2 : 4; }
 
+}  // namespace
+
+namespace flint {
+
 // Compute units of the current device, read once per device (the only state
 // the library keeps).  Falls back to 256 (MI355X) if the query fails.
 int device_cus()
@@ -59,10 +63,6 @@ int device_cus()
     cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
-
-}  // namespace
-
-namespace flint {
 
 int list_capacity(int T, int K, int E, int bm)
 {

@@ -89,6 +89,9 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
 
 int list_capacity(int T, int K, int E, int bm);
 
+// Compute units of the current device (read once per device).
+int device_cus();
+
 // ---- launches (all enqueue on `stream`, return hipGetLastError()) ----------
 
 // Number of partial logit arrays the router writes (the sum over slices of H
