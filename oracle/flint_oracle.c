@@ -356,6 +356,45 @@ void oracle_round_bf16(const double *in, double *out, int64_t n)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block-scaled 4-bit expert weights.  The pages' low-bit builds store weights
+ * in 4 bits (release news, "Availability": 4-bit weights take roughly 23 GB;
+ * Kalaris analysis: an NVFP4 build on NVIDIA hardware) without defining a
+ * format for these kernels, so the format here is a definition: OCP
+ * Microscaling MXFP4.
+ *   element  FP4 E2M1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit;
+ *            exponent field 0 is subnormal (0.m), so the magnitudes are
+ *            0, 0.5, 1, 1.5, 2, 3, 4, 6
+ *   block    32 consecutive elements of a row (along the reduction dimension)
+ *            share one scale
+ *   scale    E8M0: byte s means 2^(s - 127) for s = 0..254; 255 is NaN
+ *   packing  two elements per byte, the lower-indexed one in the low nibble
+ * A weight is element x scale, exact in float32 for every code and scale, so
+ * dequantisation returns float32 arrays that the layer functions above take
+ * unchanged. */
+static double e2m1_value(unsigned code)
+{
+    const unsigned e = (code >> 1) & 3u, m = code & 1u;
+    const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, (int)e - 1);
+    return (code & 8u) ? -mag : mag;
+}
+
+static double e8m0_value(unsigned s) { return s == 255u ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* codes [rows][cols/2], scales [rows][cols/32] -> out [rows][cols] (cols % 32 == 0). */
+int oracle_mx4_dequant(int64_t rows, int cols, const uint8_t *codes, const uint8_t *scales, float *out)
+{
+    if (rows < 0 || cols <= 0 || cols % 32 != 0 || (rows > 0 && (!codes || !scales || !out))) return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c) {
+            const unsigned byte = codes[r * (cols / 2) + c / 2];
+            const unsigned code = (c & 1) ? (byte >> 4) : (byte & 15u);
+            const unsigned sc = scales[r * (cols / 32) + c / 32];
+            out[r * cols + c] = (float)(e2m1_value(code) * e8m0_value(sc));
+        }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Parameter counts of one MoE layer from its shape, gated three-matrix experts.
  * Source: serving-kit review, "The architecture, from the config" -- the page's
  * own hand count (routed experts about 37.8B over 47 layers; six experts plus

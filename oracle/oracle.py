@@ -89,8 +89,9 @@ class Oracle:
         lib.oracle_rmsnorm.argtypes = [ctypes.c_int, ctypes.c_int, P, ctypes.c_double, P]
         lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_int64]
         lib.oracle_param_counts.argtypes = [D, P]
+        lib.oracle_mx4_dequant.argtypes = [ctypes.c_int64, ctypes.c_int, P, P, P]
         for f in ("oracle_route", "oracle_scores", "oracle_dispatch", "oracle_forward",
-                  "oracle_rmsnorm"):
+                  "oracle_rmsnorm", "oracle_mx4_dequant"):
             getattr(lib, f).restype = ctypes.c_int
         lib.oracle_round_bf16.restype = None
         lib.oracle_param_counts.restype = None
@@ -170,6 +171,29 @@ class Oracle:
         self.lib.oracle_round_bf16(_p(a), _p(out), a.size)
         return out
 
+    def mx4_dequant(self, codes, scales):
+        """Block-scaled 4-bit weights (MXFP4, see flint_oracle.c) to float32:
+        codes uint8 [..., n/2], scales uint8 [..., n/32] -> [..., n]."""
+        codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+        scales = np.ascontiguousarray(np.asarray(scales, dtype=np.uint8))
+        n = codes.shape[-1] * 2
+        if scales.shape[:-1] != codes.shape[:-1] or scales.shape[-1] * 32 != n:
+            raise ValueError("mx4_dequant: codes [..., n/2] and scales [..., n/32] disagree")
+        rows = int(np.prod(codes.shape[:-1], dtype=np.int64))
+        out = np.zeros(codes.shape[:-1] + (n,), np.float32)
+        _check(self.lib.oracle_mx4_dequant(rows, n, _p(codes), _p(scales), _p(out)), "oracle_mx4_dequant")
+        return out
+
+    def mx4_weights(self, w):
+        """A layer's weights with the expert matrices in MXFP4 (keys <name>_q and
+        <name>_s for gate, up, down and, when present, the shared expert's) ->
+        the float32 weights dict that forward() takes (router and bias as given)."""
+        out = {"router": w["router"], "bias": w.get("bias")}
+        for name in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down"):
+            if w.get(name + "_q") is not None:
+                out[name] = self.mx4_dequant(w[name + "_q"], w[name + "_s"])
+        return out
+
     def threads(self) -> int:
         """Threads the oracle's OpenMP loops use."""
         return int(self.lib.oracle_threads())
@@ -217,3 +241,11 @@ def round_bf16(a):
 
 def param_counts(d):
     return default().param_counts(d)
+
+
+def mx4_dequant(codes, scales):
+    return default().mx4_dequant(codes, scales)
+
+
+def mx4_weights(w):
+    return default().mx4_weights(w)

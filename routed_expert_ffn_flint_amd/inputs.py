@@ -12,9 +12,16 @@ here, so every tensor is drawn):
   prefill4096  T=4096,  same layer, no router bias,                   seed 0
   skew16384    T=16384, same layer, Zipf(1.1) per-expert router bias, seed 0
   stack47      T=256,   47 distinct layers, RMSNorm between layers,   seed 1
+  decode32_mx4 decode32 with every expert matrix stored as MXFP4 (block-scaled
+               4-bit, see mx4_quantize); router bf16
 
 Weights ~ N(0, 0.02^2), hidden states ~ N(0, 1), drawn in float32 and rounded
 to bf16 (round-to-nearest-even, torch's conversion) for the bf16 workloads.
+
+The 4-bit workloads store the drawn expert matrices in the block-scaled 4-bit
+format the kernels read (mx4_quantize: a storage encoding of the drawn
+values, done once when the weights are made; the layer's arithmetic starts
+from the stored codes, which the GPU path and the oracle each decode).
 
 Each tensor has its own generator, seeded from (seed, layer, tensor id), so a
 layer can be drawn without drawing the ones before it, and a tensor can be
@@ -43,6 +50,7 @@ class Workload:
     seed: int
     zipf_bias: bool = False
     layers: int = 1
+    mx4: bool = False  # expert matrices stored as MXFP4 (router stays bf16)
 
     @property
     def torch_dtype(self):
@@ -55,7 +63,10 @@ WORKLOADS = {
     "prefill4096": Workload("prefill4096", 4096, 2048, 256, 6, 512, 1024, True, 0),
     "skew16384": Workload("skew16384", 16384, 2048, 256, 6, 512, 1024, True, 0, zipf_bias=True),
     "stack47": Workload("stack47", 256, 2048, 256, 6, 512, 1024, True, 1, layers=47),
+    "decode32_mx4": Workload("decode32_mx4", 32, 2048, 256, 6, 512, 1024, True, 0, mx4=True),
 }
+
+EXPERT_MATRICES = ("gate", "up", "down", "shared_gate", "shared_up", "shared_down")
 
 WEIGHT_STD = 0.02
 ZIPF_S = 1.1
@@ -100,6 +111,42 @@ def zipf_bias(n_experts: int, seed: int) -> np.ndarray:
     return (ZIPF_SCALE * np.log(n_experts * p)).astype(np.float32)
 
 
+def mx4_quantize(w: torch.Tensor):
+    """Store a weight matrix in OCP Microscaling MXFP4, blocks of 32 along the
+    last (reduction) dimension.  Returns (codes uint8 [..., n/2], scales uint8
+    [..., n/32]).
+
+    Per block: shared exponent X = floor(log2(max |w|)) - 2 (2 is the largest
+    exponent of an E2M1 element), scale byte X + 127 (an all-zero block gets
+    byte 0); elements w / 2^X go to the nearest E2M1 magnitude
+    (0, 0.5, 1, 1.5, 2, 3, 4, 6; halfway cases to the code with a zero
+    mantissa bit, i.e. the even code), saturating at 6; the sign goes to bit 3.
+    Two elements per byte, the lower-indexed one in the low nibble."""
+    n = w.shape[-1]
+    if n % 32:
+        raise ValueError("mx4_quantize: the last dimension must be a multiple of 32")
+    lead = w.shape[:-1]
+    codes = torch.empty(lead + (n // 2,), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(lead + (n // 32,), dtype=torch.uint8, device=w.device)
+    wf_all = w.reshape(-1, n)
+    cf, sf = codes.view(-1, n // 2), scales.view(-1, n // 32)
+    rows = max(1, (1 << 24) // n)
+    for r0 in range(0, wf_all.shape[0], rows):
+        wf = wf_all[r0:r0 + rows].float().view(-1, n // 32, 32)
+        amax = wf.abs().amax(-1)
+        X = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127.0))
+        X = X.clamp(-127, 127)
+        q = wf / torch.exp2(X).unsqueeze(-1)
+        m = q.abs()
+        idx = ((m > 0.25).to(torch.uint8) + (m >= 0.75) + (m > 1.25) + (m >= 1.75) + (m > 2.5) + (m >= 3.5)
+               + (m > 5.0))
+        code = idx | ((q < 0).to(torch.uint8) << 3)
+        code = code.view(code.shape[0], n)
+        cf[r0:r0 + rows] = code[:, 0::2] | (code[:, 1::2] << 4)
+        sf[r0:r0 + rows] = (X + 127).to(torch.uint8)
+    return codes, scales
+
+
 def make_layer(wl: Workload, layer: int = 0, device="cpu", with_shared: bool = True) -> dict:
     """Weights of one layer as torch tensors on ``device``.
 
@@ -122,6 +169,11 @@ def make_layer(wl: Workload, layer: int = 0, device="cpu", with_shared: bool = T
         w["shared_gate"] = _normal((Is, H), WEIGHT_STD, dt, s, layer, "shared_gate", device)
         w["shared_up"] = _normal((Is, H), WEIGHT_STD, dt, s, layer, "shared_up", device)
         w["shared_down"] = _normal((H, Is), WEIGHT_STD, dt, s, layer, "shared_down", device)
+    if wl.mx4:
+        # stored as MXFP4: <name>_q codes and <name>_s scales replace <name>
+        for name in EXPERT_MATRICES:
+            if name in w:
+                w[name + "_q"], w[name + "_s"] = mx4_quantize(w.pop(name))
     return w
 
 
@@ -132,8 +184,8 @@ def make_tokens(wl: Workload, T: int | None = None, device="cpu", stream: int = 
 
 
 def custom(name="custom", T=8, hidden=64, n_experts=8, top_k=2, inter=64, shared_inter=64,
-           bf16=True, seed=0, zipf=False, layers=1) -> Workload:
-    return Workload(name, T, hidden, n_experts, top_k, inter, shared_inter, bf16, seed, zipf, layers)
+           bf16=True, seed=0, zipf=False, layers=1, mx4=False) -> Workload:
+    return Workload(name, T, hidden, n_experts, top_k, inter, shared_inter, bf16, seed, zipf, layers, mx4)
 
 
 def expected_distinct_experts(T: int, E: int = 256, K: int = 6) -> float:
@@ -150,4 +202,4 @@ def to_numpy_f32(t: torch.Tensor | None):
 
 
 __all__ = ["Workload", "WORKLOADS", "make_layer", "make_tokens", "zipf_bias", "custom",
-           "expected_distinct_experts", "to_numpy_f32"]
+           "expected_distinct_experts", "to_numpy_f32", "mx4_quantize", "EXPERT_MATRICES"]

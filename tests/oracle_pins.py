@@ -349,8 +349,61 @@ def pin_rmsnorm(orc):
     np.testing.assert_array_equal(orc.rmsnorm(x, 1e-6), brute.bf16_round(ref.numpy()).astype(np.float32))
 
 
+# --------------------------------------------------------------------------
+# Block-scaled 4-bit weights (OCP Microscaling MXFP4, the format the oracle
+# defines for the low-bit workloads): values fixed by the format's definition.
+
+# FP4 E2M1 code -> value, as the OCP MX v1.0 specification tabulates it
+# (codes 0-7 positive, 8-15 the same magnitudes negated).
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def _mx4_row(codes16, scale):
+    """One 32-element block (codes16: 32 codes, low-indexed in the low nibble)."""
+    c = np.asarray(codes16, np.uint8)
+    packed = (c[0::2] | (c[1::2] << 4)).astype(np.uint8)[None, :]
+    return packed, np.array([[scale]], np.uint8)
+
+
+def pin_mx4_element_table(orc):
+    codes = list(range(16)) * 2
+    q, s = _mx4_row(codes, 127)  # scale 2^0
+    got = orc.mx4_dequant(q, s)[0]
+    want = np.array(E2M1_TABLE * 2, np.float32)
+    np.testing.assert_array_equal(got, want)
+    assert all(np.signbit(got[8:16]))  # codes 8-15 carry the sign, including -0
+
+
+def pin_mx4_scale(orc):
+    # E8M0 byte b means 2^(b-127); 255 is NaN.  Code 2 is 1.0, code 7 is 6.0.
+    for b in (0, 1, 100, 127, 200, 254):
+        q, s = _mx4_row([2, 7] * 16, b)
+        got = orc.mx4_dequant(q, s)[0]
+        assert got[0] == np.float32(math.ldexp(1.0, b - 127)), (b, got[0])
+        assert got[1] == np.float32(6.0 * math.ldexp(1.0, b - 127)), (b, got[1])
+    q, s = _mx4_row([2] * 32, 255)
+    assert np.all(np.isnan(orc.mx4_dequant(q, s)))
+
+
+def pin_mx4_layout(orc):
+    # Two rows of two blocks each; element 2i in the low nibble of byte i.
+    # Row 0: block 0 scale 2^-3, block 1 scale 2^2; row 1: 2^0 and 2^-1.
+    # Element j of each block takes code (j + row) % 16.
+    scales = np.array([[124, 129], [127, 126]], np.uint8)
+    codes = np.zeros((2, 64), np.uint8)
+    want = np.zeros((2, 64), np.float32)
+    for r in range(2):
+        for j in range(64):
+            c = (j % 32 + r) % 16
+            codes[r, j] = c
+            want[r, j] = E2M1_TABLE[c] * 2.0 ** (int(scales[r, j // 32]) - 127)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    np.testing.assert_array_equal(orc.mx4_dequant(packed, scales), want)
+    assert packed[0, 0] == 0x10  # hand check of the packing: elements 0 (code 0) and 1 (code 1)
+
+
 ALL_PINS = [pin_param_counts, pin_bf16_rounding, pin_routing_hand_top2, pin_routing_hand_all,
             pin_routing_equal_logits, pin_routing_tie_break, pin_routing_limits, pin_routing_bias,
             pin_routing_library, pin_expert_closed_form, pin_bf16_intermediate, pin_dense_mixture,
             pin_shared_split, pin_token_permutation, pin_dispatch_hand, pin_dispatch_invariants,
-            pin_rmsnorm]
+            pin_rmsnorm, pin_mx4_element_table, pin_mx4_scale, pin_mx4_layout]

@@ -60,6 +60,10 @@ MUTANTS = [
     ("unweighted_gate_input", "g += (double)wg[(size_t)i * H + k] * (double)x[k];",
      "g += (double)wg[(size_t)k * width + i] * (double)x[k];"),
     ("rms_without_mean", "double r = 1.0 / sqrt(ss / (double)H + eps);", "double r = 1.0 / sqrt(ss + eps);"),
+    ("mx4_high_nibble_first", "(c & 1) ? (byte >> 4) : (byte & 15u)", "(c & 1) ? (byte & 15u) : (byte >> 4)"),
+    ("mx4_scale_bias_128", "ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
+    ("mx4_no_subnormal", "e == 0 ? 0.5 * m", "e == 0 ? 1.0 * m"),
+    ("mx4_element_bias_0", "ldexp(1.0 + 0.5 * m, (int)e - 1)", "ldexp(1.0 + 0.5 * m, (int)e)"),
 ]
 
 
