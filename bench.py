@@ -44,6 +44,7 @@ CSRC = os.path.join(ROOT, "routed_expert_ffn_flint_amd", "csrc")
 # the sources each gate/up kernel is built from
 KERNEL_SOURCES = {
     "k_expert_stream": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream.hip"],
+    "k_expert_stream_mx4": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream_mx4.hip"],
     "k_tiled": ["common.hpp", "gemm_core.hpp", "launch.hpp", "tiled.hip"],
 }
 STREAM_MAX_T = 512  # largest batch the library serves with the streaming kernels
@@ -139,11 +140,12 @@ def algorithmic(wl, idx_np):
     read once; outputs written once (float32 out)."""
     T, H, E, K, I, Is = wl.T, wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter
     eb = 2 if wl.bf16 else 4
+    wb = (0.5 + 1.0 / 32) if wl.mx4 else eb  # bytes per expert weight (MXFP4: half-byte code + 1/32 scale)
     distinct = len(np.unique(idx_np))
-    gate_up_bytes = distinct * 2 * I * H * eb + 2 * Is * H * eb + T * H * eb + (T * K * I + T * Is) * eb
-    down_bytes = distinct * H * I * eb + Is * H * eb + (T * K * I + T * Is) * eb + (T * K + T) * H * 4
+    gate_up_bytes = distinct * 2 * I * H * wb + 2 * Is * H * wb + T * H * eb + (T * K * I + T * Is) * eb
+    down_bytes = distinct * H * I * wb + Is * H * wb + (T * K * I + T * Is) * eb + (T * K + T) * H * 4
     router_bytes = E * H * eb + T * H * eb
-    layer_bytes = (E * H + distinct * 3 * I * H + 3 * Is * H) * eb + T * H * eb + T * H * 4
+    layer_bytes = E * H * eb + (distinct * 3 * I * H + 3 * Is * H) * wb + T * H * eb + T * H * 4
     flops = {
         "router": 2 * T * E * H,
         "gate_up": 4 * T * K * I * H + 4 * T * Is * H,
@@ -163,7 +165,11 @@ def cpu_baseline(wl, w_dev, x_dev, target_s):
 
     o = orc.default()
     d = orc.dims(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, wl.bf16)
-    wh = {k: inputs.to_numpy_f32(v) for k, v in w_dev.items()}
+    if wl.mx4:  # the oracle decodes the stored 4-bit weights itself
+        wh = o.mx4_weights({k: (v.cpu().numpy() if k.endswith(("_q", "_s")) else inputs.to_numpy_f32(v))
+                            for k, v in w_dev.items()})
+    else:
+        wh = {k: inputs.to_numpy_f32(v) for k, v in w_dev.items()}
     n_tok = min(wl.T, 32)
     xh = inputs.to_numpy_f32(x_dev[:n_tok])
     reps, t0 = 0, time.perf_counter()
@@ -200,7 +206,7 @@ def main():
     stack = wl.layers > 1
     n_copies = wl.layers if stack else max(1, args.copies)
     layers = [inputs.make_layer(wl, c, dev) for c in range(n_copies)]
-    wstructs = [api.weights_struct(d, w) for w in layers]
+    wstructs = [api.weights_mx4_struct(d, w) if wl.mx4 else api.weights_struct(d, w) for w in layers]
     x = inputs.make_tokens(wl, device=dev)
     T = wl.T
     ws = api.workspace(d, T, dev)
@@ -216,10 +222,13 @@ def main():
     xp = ctypes.c_void_p(x.data_ptr())
 
     def layer_call(c, xin, events=None):
-        if events is None:
+        arr = None if events is None else (ctypes.c_void_p * 10)(*[e.value for e in events])
+        if wl.mx4:
+            st = lib.flint_moe_forward_mx4(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp,
+                                           wsp, wsn, sp, arr)
+        elif events is None:
             st = lib.flint_moe_forward(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp, wsp, wsn, sp)
         else:
-            arr = (ctypes.c_void_p * 10)(*[e.value for e in events])
             st = lib.flint_moe_forward_profiled(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp,
                                                 wsp, wsn, sp, arr)
         if st != 0:
@@ -329,7 +338,7 @@ def main():
     layer_flops = float(np.mean([p["flops"]["layer"] for p in per_copy]))
     gu_flops = float(np.mean([p["flops"]["gate_up"] for p in per_copy]))
     big = T >= 2048
-    kernel = "k_expert_stream" if T <= STREAM_MAX_T else "k_tiled"
+    kernel = ("k_expert_stream_mx4" if wl.mx4 else "k_expert_stream") if T <= STREAM_MAX_T else "k_tiled"
     digest = sources_digest(kernel)
     traffic = counters_traffic(kernel, wl.name, digest)
     kname = f"{kernel}<gate/up> (grouped gate/up GEMM + SwiGLU, routed and shared)"
@@ -359,7 +368,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {'47 stacked' if stack else 'one'} Flint MoE layer(s), T={T}, "
                                f"H={wl.hidden}, E={wl.n_experts} top-{wl.top_k}, I={wl.inter}, "
-                               f"Is={wl.shared_inter}", "T": T, "weight_copies": n_copies,
+                               f"Is={wl.shared_inter}" + (", expert weights MXFP4" if wl.mx4 else ""),
+                   "T": T, "weight_copies": n_copies,
                    "graph": bool(graph is not None), "wall_s": wall},
         "roofline": roofline,
         "layer_roofline": layer,

@@ -160,6 +160,44 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *dims, int32_t T, c
                                         float *topk_w_out, void *ws, size_t ws_bytes, void *stream,
                                         void *const *events);
 
+/* ---- Expert weights in MXFP4 (block-scaled 4-bit) --------------------------
+ * The pages' low-bit builds store weights in 4 bits (release news,
+ * "Availability": 4-bit weights take roughly 23 GB) without a format for these
+ * kernels; this library defines one: OCP Microscaling MXFP4.  Each expert
+ * matrix (routed and shared) is stored as
+ *   codes  [rows][cols/2] bytes: FP4 E2M1 elements (sign, 2 exponent bits with
+ *          bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two
+ *          per byte, the lower-indexed element in the low nibble;
+ *   scales [rows][cols/32] bytes: one E8M0 scale per 32 consecutive elements of
+ *          a row, value 2^(s - 127) (255 is NaN);
+ * where rows x cols is the bf16 layout above (gate/up [E][I][H] -> codes
+ * [E][I][H/2], scales [E][I][H/32]; down [E][H][I] -> [E][H][I/2], [E][H][I/32];
+ * the shared matrices likewise).  A weight is element x scale.  The router
+ * stays in dims.dtype (BF16), activations are bf16, and everything after the
+ * weight decoding is as in flint_moe_forward. */
+typedef struct {
+    const void *router;        /* [E][H] bf16 */
+    const float *router_bias;  /* [E] or NULL */
+    const uint8_t *gate_q, *gate_s;
+    const uint8_t *up_q, *up_s;
+    const uint8_t *down_q, *down_s;
+    const uint8_t *shared_gate_q, *shared_gate_s;  /* NULL when shared_inter == 0 */
+    const uint8_t *shared_up_q, *shared_up_s;
+    const uint8_t *shared_down_q, *shared_down_s;
+} flint_moe_weights_mx4;
+
+/* flint_moe_forward with MXFP4 expert weights.  Same arguments and results as
+ * flint_moe_forward otherwise; the workspace is flint_moe_workspace_bytes(dims,
+ * T).  Supported: dims.dtype == FLINT_BF16, T <= 512, H a multiple of 1024, I
+ * and Is multiples of 512 (Is may be 0), 16-byte aligned code arrays; anything
+ * else is refused with FLINT_UNSUPPORTED.  `events` as in
+ * flint_moe_forward_profiled (10 handles) or NULL. */
+flint_status flint_moe_forward_mx4(const flint_moe_dims *dims, int32_t T, const void *x,
+                                   const flint_moe_weights_mx4 *weights, void *out,
+                                   flint_dtype out_dtype, int32_t *topk_idx_out,
+                                   float *topk_w_out, void *ws, size_t ws_bytes, void *stream,
+                                   void *const *events);
+
 /* RMSNorm between stacked MoE layers (unit gain): out = bf16(in / sqrt(mean(in^2) + eps)),
  * the mean over each row of H values.  in [T][H] float32, out [T][H] bf16.
  * H must be a multiple of 64 and at most 8192.  This joins consecutive layers in

@@ -29,8 +29,14 @@ class Weights(ctypes.Structure):
                 ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p)]
 
 
+class WeightsMx4(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p)] + [
+        (f"{name}_{part}", ctypes.c_void_p)
+        for name in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down") for part in ("q", "s")]
+
+
 EXPORTS = ("flint_status_string", "flint_moe_workspace_bytes", "flint_moe_route", "flint_moe_dispatch",
-           "flint_moe_forward", "flint_moe_forward_profiled", "flint_rmsnorm")
+           "flint_moe_forward", "flint_moe_forward_profiled", "flint_moe_forward_mx4", "flint_rmsnorm")
 
 
 def load():
@@ -57,6 +63,8 @@ def load():
     lib.flint_moe_forward.restype = I32
     lib.flint_moe_forward_profiled.argtypes = [D, I32, P, ctypes.POINTER(Weights), P, I32, P, P, P, SZ, P, P]
     lib.flint_moe_forward_profiled.restype = I32
+    lib.flint_moe_forward_mx4.argtypes = [D, I32, P, ctypes.POINTER(WeightsMx4), P, I32, P, P, P, SZ, P, P]
+    lib.flint_moe_forward_mx4.restype = I32
     lib.flint_rmsnorm.argtypes = [I32, I32, P, P, ctypes.c_float, P]
     lib.flint_rmsnorm.restype = I32
     _lib = lib

@@ -12,7 +12,7 @@ import ctypes
 
 import torch
 
-from ._lib import Dims, Weights, load
+from ._lib import Dims, Weights, WeightsMx4, load
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, DEVICE_ERROR = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
@@ -154,6 +154,49 @@ def flint_moe_forward(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=No
         raise FlintError(st, "flint_moe_forward" if events is None else "flint_moe_forward_profiled")
 
 
+def weights_mx4_struct(d: Dims, w: dict) -> WeightsMx4:
+    """MXFP4 expert weights (keys <name>_q codes and <name>_s scales, uint8; see
+    inputs.mx4_quantize) plus the bf16 router and optional bias."""
+    E, H, I, Is = d.n_experts, d.hidden, d.inter, d.shared_inter
+    _check_tensor("router", w["router"], torch.bfloat16, (E, H))
+    _check_tensor("router_bias", w.get("bias"), torch.float32, (E,))
+    shapes = {"gate": (E, I, H), "up": (E, I, H), "down": (E, H, I)}
+    if Is > 0:
+        shapes.update({"shared_gate": (Is, H), "shared_up": (Is, H), "shared_down": (H, Is)})
+    ptrs = {}
+    for name, shp in shapes.items():
+        _check_tensor(name + "_q", w[name + "_q"], torch.uint8, shp[:-1] + (shp[-1] // 2,))
+        _check_tensor(name + "_s", w[name + "_s"], torch.uint8, shp[:-1] + (shp[-1] // 32,))
+        ptrs[name + "_q"], ptrs[name + "_s"] = _ptr(w[name + "_q"]), _ptr(w[name + "_s"])
+    return WeightsMx4(router=_ptr(w["router"]), router_bias=_ptr(w.get("bias")), **ptrs)
+
+
+def flint_moe_forward_mx4(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=None, ws=None, stream=None,
+                          events=None):
+    """flint_moe_forward with MXFP4 expert weights: ``weights`` is a dict (see
+    weights_mx4_struct) or a prepared WeightsMx4; events as in flint_moe_forward."""
+    T = x.shape[0]
+    _check_tensor("x", x, torch.bfloat16, (T, d.hidden))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check_tensor("out", out, None, (T, d.hidden))
+    _check_tensor("topk_idx_out", topk_idx_out, torch.int32, (T, d.top_k))
+    _check_tensor("topk_w_out", topk_w_out, torch.float32, (T, d.top_k))
+    _check_tensor("ws", ws, torch.uint8)
+    ws_struct = weights if isinstance(weights, WeightsMx4) else weights_mx4_struct(d, weights)
+    out_dt = BF16 if out.dtype == torch.bfloat16 else F32
+    arr = None
+    if events is not None:
+        if len(events) != 10:
+            raise ValueError("events: 10 hipEvent_t handles (start/stop of 5 stages)")
+        arr = (ctypes.c_void_p * 10)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
+    st = load().flint_moe_forward_mx4(ctypes.byref(d), T, _ptr(x), ctypes.byref(ws_struct), _ptr(out), out_dt,
+                                      _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream), arr)
+    if st != OK:
+        raise FlintError(st, "flint_moe_forward_mx4")
+
+
 def flint_rmsnorm(inp, out, eps=1e-6, stream=None):
     T, H = inp.shape
     _check_tensor("in", inp, torch.float32, (T, H))
@@ -166,13 +209,17 @@ def flint_rmsnorm(inp, out, eps=1e-6, stream=None):
 # ---- convenience: allocate outputs with torch, then call the entry points ----
 
 def forward(d: Dims, x, weights, out_dtype=torch.float32, ws=None, stream=None, return_routing=False):
+    """The layer; MXFP4 weight dicts (keys ending in _q/_s) go to flint_moe_forward_mx4."""
     T = x.shape[0]
     out = torch.empty((T, d.hidden), dtype=out_dtype, device=x.device)
     idx = torch.empty((T, d.top_k), dtype=torch.int32, device=x.device) if return_routing else None
     tw = torch.empty((T, d.top_k), dtype=torch.float32, device=x.device) if return_routing else None
     if ws is None:
         ws = workspace(d, T, x.device)
-    flint_moe_forward(d, x, weights, out, idx, tw, ws, stream)
+    if isinstance(weights, WeightsMx4) or (isinstance(weights, dict) and "gate_q" in weights):
+        flint_moe_forward_mx4(d, x, weights, out, idx, tw, ws, stream)
+    else:
+        flint_moe_forward(d, x, weights, out, idx, tw, ws, stream)
     return (out, idx, tw) if return_routing else out
 
 

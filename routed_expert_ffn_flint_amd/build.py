@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libflint_moe.so")
-SOURCES = ["route.hip", "expert.hip", "stream.hip", "tiled.hip", "abi.cpp"]
+SOURCES = ["route.hip", "expert.hip", "stream.hip", "stream_mx4.hip", "tiled.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 

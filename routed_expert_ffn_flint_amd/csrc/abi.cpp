@@ -235,29 +235,15 @@ flint_status flint_moe_forward(const flint_moe_dims *d, int32_t T, const void *x
                                       nullptr);
 }
 
-flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, const void *x,
-                                        const flint_moe_weights *wt, void *out, flint_dtype out_dtype,
-                                        int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
-                                        void *stream, void *const *events)
-{
-    flint_status st = check_dims(d);
-    if (st != FLINT_OK) return st;
-    if ((st = check_T(d, T)) != FLINT_OK) return st;
-    if (out_dtype != FLINT_F32 && out_dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
-    if (T == 0) return FLINT_OK;
-    if (!x || !wt || !out || !wt->router || !wt->gate || !wt->up || !wt->down) return FLINT_INVALID_ARG;
-    const bool has_shared = d->shared_inter > 0;
-    if (has_shared && (!wt->shared_gate || !wt->shared_up || !wt->shared_down)) return FLINT_INVALID_ARG;
-    const void *ptrs[] = {x, out, wt->router, wt->gate, wt->up, wt->down};
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return FLINT_UNSUPPORTED;
-    if (wt->router_bias && !aligned16(wt->router_bias)) return FLINT_UNSUPPORTED;
-    if (has_shared && (!aligned16(wt->shared_gate) || !aligned16(wt->shared_up) || !aligned16(wt->shared_down)))
-        return FLINT_UNSUPPORTED;
-    if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
-        return FLINT_UNSUPPORTED;
-    if ((st = check_ws(d, T, ws, ws_bytes)) != FLINT_OK) return st;
+}  // extern "C"
 
+// The layer's launches once the arguments are checked: router, top-k +
+// dispatch, expert stages, combine.  `e` arrives with the weight pointers set.
+static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void *x, const void *router,
+                                 const float *router_bias, ExpertArgs e, void *out, flint_dtype out_dtype,
+                                 int32_t *topk_idx_out, float *topk_w_out, void *ws, void *stream,
+                                 void *const *events)
+{
     hipStream_t s = (hipStream_t)stream;
     const bool bf16 = d->dtype == FLINT_BF16;
     Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
@@ -268,8 +254,8 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
         for (int i = 0; i < 5; ++i) marks[i] = Marks{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]};
     const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
                                                d->dtype == FLINT_BF16);
-    if (launch_router_logits(bf16, x, T, d->hidden, wt->router, wt->router_bias, d->n_experts, w.logits, s,
-                             marks[0]) != hipSuccess)
+    if (launch_router_logits(bf16, x, T, d->hidden, router, router_bias, d->n_experts, w.logits, s, marks[0]) !=
+        hipSuccess)
         return FLINT_DEVICE_ERROR;
 
     DispatchArgs a = dispatch_args(d, T, w);
@@ -284,7 +270,6 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     a.slot_of = w.slot_of;
     if (launch_topk_dispatch(a, s, marks[1]) != hipSuccess) return FLINT_DEVICE_ERROR;
 
-    ExpertArgs e{};
     e.bf16 = bf16;
     e.T = T;
     e.H = d->hidden;
@@ -293,12 +278,6 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     e.I = d->inter;
     e.Is = d->shared_inter;
     e.x = x;
-    e.gate = wt->gate;
-    e.up = wt->up;
-    e.down = wt->down;
-    e.shared_gate = wt->shared_gate;
-    e.shared_up = wt->shared_up;
-    e.shared_down = wt->shared_down;
     e.sorted_token = w.sorted_token;
     e.offsets = w.offsets;
     e.slot_of = w.slot_of;
@@ -316,6 +295,97 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     e.cus = device_cus();
     if (launch_experts(e, s, events ? marks + 2 : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
     return FLINT_OK;
+}
+
+// Checks shared by both forward entry points (everything but the weights).
+static flint_status check_forward(const flint_moe_dims *d, int32_t T, const void *x, const void *router,
+                                  const float *router_bias, void *out, flint_dtype out_dtype,
+                                  int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes)
+{
+    flint_status st = check_dims(d);
+    if (st != FLINT_OK) return st;
+    if ((st = check_T(d, T)) != FLINT_OK) return st;
+    if (out_dtype != FLINT_F32 && out_dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
+    if (T == 0) return FLINT_OK;
+    if (!x || !out || !router) return FLINT_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(router)) return FLINT_UNSUPPORTED;
+    if (router_bias && !aligned16(router_bias)) return FLINT_UNSUPPORTED;
+    if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
+        return FLINT_UNSUPPORTED;
+    return check_ws(d, T, ws, ws_bytes);
+}
+
+extern "C" {
+
+flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, const void *x,
+                                        const flint_moe_weights *wt, void *out, flint_dtype out_dtype,
+                                        int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                                        void *stream, void *const *events)
+{
+    flint_status st = check_forward(d, T, x, wt ? wt->router : nullptr, wt ? wt->router_bias : nullptr, out,
+                                    out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes);
+    if (st != FLINT_OK || T == 0) return st;
+    if (!wt->gate || !wt->up || !wt->down) return FLINT_INVALID_ARG;
+    const bool has_shared = d->shared_inter > 0;
+    if (has_shared && (!wt->shared_gate || !wt->shared_up || !wt->shared_down)) return FLINT_INVALID_ARG;
+    if (!aligned16(wt->gate) || !aligned16(wt->up) || !aligned16(wt->down)) return FLINT_UNSUPPORTED;
+    if (has_shared && (!aligned16(wt->shared_gate) || !aligned16(wt->shared_up) || !aligned16(wt->shared_down)))
+        return FLINT_UNSUPPORTED;
+    ExpertArgs e{};
+    e.gate = wt->gate;
+    e.up = wt->up;
+    e.down = wt->down;
+    e.shared_gate = wt->shared_gate;
+    e.shared_up = wt->shared_up;
+    e.shared_down = wt->shared_down;
+    return launch_layer(d, T, x, wt->router, wt->router_bias, e, out, out_dtype, topk_idx_out, topk_w_out, ws,
+                        stream, events);
+}
+
+flint_status flint_moe_forward_mx4(const flint_moe_dims *d, int32_t T, const void *x,
+                                   const flint_moe_weights_mx4 *wt, void *out, flint_dtype out_dtype,
+                                   int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                                   void *stream, void *const *events)
+{
+    flint_status st = check_dims(d);
+    if (st != FLINT_OK) return st;
+    if (d->dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
+    if (T > kMx4MaxT || !mx4_eligible(T, d->hidden, d->inter, d->shared_inter)) return FLINT_UNSUPPORTED;
+    // the kernels use the workspace's tile lists with their own row tiles
+    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                                               true);
+    if (tiles.bm1 != mx4_bm() || tiles.bm2 != mx4_bm()) return FLINT_UNSUPPORTED;
+    st = check_forward(d, T, x, wt ? wt->router : nullptr, wt ? wt->router_bias : nullptr, out, out_dtype,
+                       topk_idx_out, topk_w_out, ws, ws_bytes);
+    if (st != FLINT_OK || T == 0) return st;
+    const bool has_shared = d->shared_inter > 0;
+    const uint8_t *need[] = {wt->gate_q, wt->gate_s, wt->up_q, wt->up_s, wt->down_q, wt->down_s};
+    for (const uint8_t *p : need)
+        if (!p) return FLINT_INVALID_ARG;
+    const uint8_t *need_shared[] = {wt->shared_gate_q, wt->shared_gate_s, wt->shared_up_q,
+                                    wt->shared_up_s,   wt->shared_down_q, wt->shared_down_s};
+    if (has_shared)
+        for (const uint8_t *p : need_shared)
+            if (!p) return FLINT_INVALID_ARG;
+    if (!aligned16(wt->gate_q) || !aligned16(wt->up_q) || !aligned16(wt->down_q)) return FLINT_UNSUPPORTED;
+    if (has_shared && (!aligned16(wt->shared_gate_q) || !aligned16(wt->shared_up_q) || !aligned16(wt->shared_down_q)))
+        return FLINT_UNSUPPORTED;
+    ExpertArgs e{};
+    e.mx4 = true;
+    e.gate = wt->gate_q;
+    e.up = wt->up_q;
+    e.down = wt->down_q;
+    e.gate_s = wt->gate_s;
+    e.up_s = wt->up_s;
+    e.down_s = wt->down_s;
+    e.shared_gate = wt->shared_gate_q;
+    e.shared_up = wt->shared_up_q;
+    e.shared_down = wt->shared_down_q;
+    e.shared_gate_s = wt->shared_gate_s;
+    e.shared_up_s = wt->shared_up_s;
+    e.shared_down_s = wt->shared_down_s;
+    return launch_layer(d, T, x, wt->router, wt->router_bias, e, out, out_dtype, topk_idx_out, topk_w_out, ws,
+                        stream, events);
 }
 
 flint_status flint_rmsnorm(int32_t T, int32_t H, const float *in, void *out_bf16, float eps, void *stream)

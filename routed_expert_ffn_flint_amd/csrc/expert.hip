@@ -307,6 +307,11 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
     const ExpertTiles &t = a.tiles;
     const Marks m1 = marks ? marks[0] : Marks{}, m2 = marks ? marks[1] : Marks{}, m3 = marks ? marks[2] : Marks{};
     const dim3 gc(a.T, (a.H + 1023) / 1024);
+    if (a.mx4) {
+        const hipError_t err = launch_experts_mx4(a, stream, marks);
+        if (err != hipSuccess) return err;
+        return launch_k(k_combine, gc, 256, 0, stream, m3, a);
+    }
     if (t.stream || t.tiled) {
         const hipError_t err =
             t.stream ? launch_experts_stream(a, stream, marks) : launch_experts_tiled(a, stream, marks);

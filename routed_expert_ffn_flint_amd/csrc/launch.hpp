@@ -121,10 +121,12 @@ hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks
 
 struct ExpertArgs {
     bool bf16;
+    bool mx4;  // expert matrices in MXFP4: gate/up/down/shared_* hold codes, *_s the scales
     int T, H, E, K, I, Is;
     const void *x;
     const void *gate, *up, *down;
     const void *shared_gate, *shared_up, *shared_down;
+    const uint8_t *gate_s, *up_s, *down_s, *shared_gate_s, *shared_up_s, *shared_down_s;
     const int32_t *sorted_token, *offsets, *slot_of;
     const float *topk_w;
     const int32_t *list1, *list2, *meta;
@@ -145,6 +147,13 @@ int stream_bm1();
 int stream_bm2();
 // marks (nullable): gate/up and down stages.
 hipError_t launch_experts_stream(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
+
+// Streaming kernels for MXFP4 expert weights (small batches, bf16 activations):
+// eligibility, rows per tile (both lists), launch of the gate/up and down stages.
+constexpr int kMx4MaxT = 512;
+bool mx4_eligible(int T, int H, int I, int Is);
+int mx4_bm();
+hipError_t launch_experts_mx4(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 
 // LDS-tiled kernels for large bf16 batches: rows per gate/up and per down tile
 // (128 or 256, from the mean rows per expert), eligibility, launch.

@@ -52,6 +52,45 @@ def host_weights(w: dict, experts=None) -> dict:
     return out
 
 
+def host_weights_mx4(w: dict, experts=None) -> dict:
+    """MXFP4 weights (codes and scales on the device) decoded by the oracle into
+    float32 host arrays; with ``experts`` given, only those experts' matrices
+    (the rest stay zero), as in host_weights."""
+    out = {"router": inputs.to_numpy_f32(w["router"]), "bias": inputs.to_numpy_f32(w.get("bias"))}
+    for k in ("shared_gate", "shared_up", "shared_down"):
+        if w.get(k + "_q") is not None:
+            out[k] = orc.mx4_dequant(w[k + "_q"].cpu().numpy(), w[k + "_s"].cpu().numpy())
+    for k in ("gate", "up", "down"):
+        q, sc = w[k + "_q"], w[k + "_s"]
+        shape = tuple(q.shape[:-1]) + (q.shape[-1] * 2,)
+        if experts is None:
+            out[k] = orc.mx4_dequant(q.cpu().numpy(), sc.cpu().numpy())
+        else:
+            full = np.zeros(shape, np.float32)
+            ex = torch.as_tensor(np.asarray(sorted(experts)), device=q.device, dtype=torch.long)
+            if len(ex):
+                full[ex.cpu().numpy()] = orc.mx4_dequant(q.index_select(0, ex).cpu().numpy(),
+                                                          sc.index_select(0, ex).cpu().numpy())
+            out[k] = full
+    return out
+
+
+def parity_mx4(wl, w_dev, x_dev, out_dtype=torch.float32):
+    """Every token of an MXFP4 layer against the oracle run on the decoded weights."""
+    out, idx, tw = gpu_layer(wl, w_dev, x_dev, out_dtype)
+    d = oracle_dims(wl)
+    xh = inputs.to_numpy_f32(x_dev)
+    router = inputs.to_numpy_f32(w_dev["router"])
+    bias = inputs.to_numpy_f32(w_dev.get("bias"))
+    o_idx, o_w, tie = orc.route(d, xh, router, bias)
+    gi, gw = idx.cpu().numpy(), tw.cpu().numpy()
+    nties = check_routing(gi, gw, o_idx, o_w, tie, wl.name)
+    wh = host_weights_mx4(w_dev, set(gi.ravel().tolist()))
+    ref, _, _, _ = orc.forward(d, xh, wh, force_idx=gi)
+    rel = check_output(out.float().cpu().numpy(), ref, wl.name)
+    return {"near_ties": nties, "rel_err": rel, "idx": gi, "out": out}
+
+
 def check_routing(gpu_idx, gpu_w, ora_idx, ora_w, near_tie, where=""):
     """Returns the number of near-tie tokens whose sets differ."""
     gpu_idx = np.asarray(gpu_idx)

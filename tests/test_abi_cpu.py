@@ -29,7 +29,7 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(flint_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(flint_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_abi():
@@ -145,3 +145,41 @@ def test_binding_raises_on_refusal(lib):
     with pytest.raises(api.FlintError) as ei:
         api.workspace(flint_dims(top_k=9), 32, device="cpu")
     assert ei.value.status == api.UNSUPPORTED
+
+
+def _forward_mx4(lib, d, T, ws_bytes=None, w=None, ws=FAKE_WS, x=FAKE):
+    if w is None:
+        fields = {f"{n}_{p}": FAKE for n in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down")
+                  for p in ("q", "s")}
+        w = _lib.WeightsMx4(router=FAKE, router_bias=None, **fields)
+    if ws_bytes is None:
+        ws_bytes = api.flint_moe_workspace_bytes(d, T) if T >= 0 else 0
+    return lib.flint_moe_forward_mx4(ctypes.byref(d), T, x, ctypes.byref(w), FAKE, api.F32, None, None, ws,
+                                     ws_bytes, None, None)
+
+
+def test_forward_mx4_refusals(lib):
+    d = flint_dims()
+    assert _forward_mx4(lib, d, 0) == api.OK  # no-op
+    assert _forward_mx4(lib, flint_dims(dtype=api.F32), 32) == api.UNSUPPORTED  # bf16 activations only
+    assert _forward_mx4(lib, d, 513) == api.UNSUPPORTED  # small batches only
+    assert _forward_mx4(lib, flint_dims(hidden=1536), 32) == api.UNSUPPORTED  # H % 1024
+    assert _forward_mx4(lib, flint_dims(inter=256), 32) == api.UNSUPPORTED  # I % 512
+    assert _forward_mx4(lib, flint_dims(shared_inter=768), 32) == api.UNSUPPORTED  # Is % 512
+    assert _forward_mx4(lib, d, 32, x=None) == api.INVALID_ARG
+    assert _forward_mx4(lib, d, 32, ws_bytes=api.flint_moe_workspace_bytes(d, 32) - 1) == \
+        api.WORKSPACE_TOO_SMALL
+    fields = {f"{n}_{p}": FAKE for n in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down")
+              for p in ("q", "s")}
+    fields["down_s"] = None
+    assert _forward_mx4(lib, d, 32, w=_lib.WeightsMx4(router=FAKE, router_bias=None, **fields)) == \
+        api.INVALID_ARG
+    fields["down_s"] = FAKE
+    fields["gate_q"] = FAKE + 8
+    assert _forward_mx4(lib, d, 32, w=_lib.WeightsMx4(router=FAKE, router_bias=None, **fields)) == \
+        api.UNSUPPORTED  # code arrays 16-byte aligned
+    # no shared expert: its pointers may be NULL
+    ns = flint_dims(shared_inter=0)
+    fields = {f"{n}_{p}": FAKE for n in ("gate", "up", "down") for p in ("q", "s")}
+    w = _lib.WeightsMx4(router=FAKE, router_bias=None, **fields)
+    assert _forward_mx4(lib, ns, 0, w=w) == api.OK

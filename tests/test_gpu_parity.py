@@ -265,3 +265,32 @@ def test_profiled_forward_same_bits_and_ordered_stages(name):
     print(f"{name}: stages_us={[round(t * 1e3, 1) for t in stages]} span_us={total * 1e3:.1f}")
     for e in evs:
         hip.hipEventDestroy(e)
+
+
+# ---- MXFP4 expert weights (flint_moe_forward_mx4) ------------------------
+
+MX4_CASES = [
+    # name,        T,  H,    E,  K, I,   Is,  bias
+    ("mx4_t33",    33, 1024, 16, 4, 512, 512, True),
+    ("mx4_t7_ns",  7,  1024, 8,  2, 512, 0,   False),
+    ("mx4_t200",   200, 2048, 32, 6, 512, 1024, True),
+]
+
+
+@pytest.mark.parametrize("case", MX4_CASES, ids=[c[0] for c in MX4_CASES])
+def test_mx4_small_every_token(case):
+    name, T, H, E, K, I, Is, bias = case
+    wl = inputs.custom(name, T, H, E, K, I, Is, True, seed=5, zipf=bias, mx4=True)
+    w, x = _layer(wl)
+    st = G.parity_mx4(wl, w, x)
+    print(f"{name}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
+
+
+def test_mx4_decode32_every_token_and_deterministic():
+    wl = inputs.WORKLOADS["decode32_mx4"]
+    w = inputs.make_layer(wl, 0, "cuda")
+    x = inputs.make_tokens(wl, device="cuda")
+    st = G.parity_mx4(wl, w, x)
+    again, _, _ = G.gpu_layer(wl, w, x)
+    assert torch.equal(st["out"].view(torch.int32), again.view(torch.int32))
+    print(f"decode32_mx4: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
