@@ -163,18 +163,24 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *dims, int32_t T, c
 /* ---- Expert weights in MXFP4 (block-scaled 4-bit) --------------------------
  * The pages' low-bit builds store weights in 4 bits (release news,
  * "Availability": 4-bit weights take roughly 23 GB) without a format for these
- * kernels; this library defines one: OCP Microscaling MXFP4.  Each expert
- * matrix (routed and shared) is stored as
- *   codes  [rows][cols/2] bytes: FP4 E2M1 elements (sign, 2 exponent bits with
- *          bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two
- *          per byte, the lower-indexed element in the low nibble;
- *   scales [rows][cols/32] bytes: one E8M0 scale per 32 consecutive elements of
- *          a row, value 2^(s - 127) (255 is NaN);
- * where rows x cols is the bf16 layout above (gate/up [E][I][H] -> codes
- * [E][I][H/2], scales [E][I][H/32]; down [E][H][I] -> [E][H][I/2], [E][H][I/32];
- * the shared matrices likewise).  A weight is element x scale.  The router
- * stays in dims.dtype (BF16), activations are bf16, and everything after the
- * weight decoding is as in flint_moe_forward. */
+ * kernels; this library defines one: OCP Microscaling MXFP4 values in a tiled
+ * byte order.  The values: FP4 E2M1 elements (sign, 2 exponent bits with bias
+ * 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E8M0 scale
+ * 2^(s - 127) per 32 consecutive elements of a row (255 is NaN); a weight is
+ * element x scale.  The matrices are the bf16 layout's (gate/up [E][I][H],
+ * down [E][H][I], shared [Is][H], [Is][H], [H][Is]), rows x cols each, with
+ * rows a multiple of 16 and cols a multiple of 32.  Storage: a tile is 16
+ * consecutive rows x one 32-element block;
+ *   codes  [rows/16][cols/32][16][16] bytes: per tile, row r's 16 bytes (two
+ *          elements per byte, the lower-indexed in the low nibble), rows in
+ *          order, tiles along the columns, then down the rows;
+ *   scales [rows/16][cols/32][16] bytes: per tile, row r's scale byte;
+ * each expert's arrays follow the previous expert's ([E] outermost).  The byte
+ * for element (row, col) is at codes[row/16][col/32][row%16][(col%32)/2], its
+ * scale at scales[row/16][col/32][row%16].  (This order makes the 64 lanes of
+ * one GPU load read one contiguous stretch.)  The router stays in dims.dtype
+ * (BF16), activations are bf16, and everything after the weight decoding is as
+ * in flint_moe_forward. */
 typedef struct {
     const void *router;        /* [E][H] bf16 */
     const float *router_bias;  /* [E] or NULL */
@@ -190,7 +196,7 @@ typedef struct {
  * flint_moe_forward otherwise; the workspace is flint_moe_workspace_bytes(dims,
  * T).  Supported: dims.dtype == FLINT_BF16, T <= 512, H a multiple of 1024, I
  * and Is multiples of 512 (Is may be 0), 16-byte aligned code arrays; anything
- * else is refused with FLINT_UNSUPPORTED.  `events` as in
+ * else is refused with FLINT_UNSUPPORTED.  The weight arrays are read only.  `events` as in
  * flint_moe_forward_profiled (10 handles) or NULL. */
 flint_status flint_moe_forward_mx4(const flint_moe_dims *dims, int32_t T, const void *x,
                                    const flint_moe_weights_mx4 *weights, void *out,

@@ -394,6 +394,33 @@ int oracle_mx4_dequant(int64_t rows, int cols, const uint8_t *codes, const uint8
     return ORACLE_OK;
 }
 
+/* The library's storage order for these arrays (a definition, like the format):
+ * a tile is 16 consecutive rows x one 32-element block; the tiles of a matrix
+ * run along the columns, then down the rows; a tile holds its 16 rows' 16 code
+ * bytes, row after row (256 bytes), and its 16 scale bytes, row after row.
+ * Back to row-major, element by element of the definition:
+ *   codes_t[rb][kb][r][j] -> codes[rb*16 + r][kb*16 + j]
+ *   scales_t[rb][kb][r]   -> scales[rb*16 + r][kb]
+ * rows % 16 == 0, cols % 32 == 0; stacked matrices ([E][rows][cols]) are one
+ * matrix of E*rows rows, as their tile rows follow each other. */
+int oracle_mx4_untile(int64_t rows, int cols, const uint8_t *codes_t, const uint8_t *scales_t, uint8_t *codes,
+                      uint8_t *scales)
+{
+    if (rows < 0 || rows % 16 != 0 || cols <= 0 || cols % 32 != 0 ||
+        (rows > 0 && (!codes_t || !scales_t || !codes || !scales)))
+        return ORACLE_BAD_ARG;
+    const int64_t nkb = cols / 32;
+    for (int64_t rb = 0; rb < rows / 16; ++rb)
+        for (int64_t kb = 0; kb < nkb; ++kb)
+            for (int r = 0; r < 16; ++r) {
+                const int64_t tile = rb * nkb + kb;
+                for (int j = 0; j < 16; ++j)
+                    codes[(rb * 16 + r) * (cols / 2) + kb * 16 + j] = codes_t[(tile * 16 + r) * 16 + j];
+                scales[(rb * 16 + r) * nkb + kb] = scales_t[tile * 16 + r];
+            }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Parameter counts of one MoE layer from its shape, gated three-matrix experts.
  * Source: serving-kit review, "The architecture, from the config" -- the page's

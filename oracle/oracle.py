@@ -90,8 +90,9 @@ class Oracle:
         lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_int64]
         lib.oracle_param_counts.argtypes = [D, P]
         lib.oracle_mx4_dequant.argtypes = [ctypes.c_int64, ctypes.c_int, P, P, P]
+        lib.oracle_mx4_untile.argtypes = [ctypes.c_int64, ctypes.c_int, P, P, P, P]
         for f in ("oracle_route", "oracle_scores", "oracle_dispatch", "oracle_forward",
-                  "oracle_rmsnorm", "oracle_mx4_dequant"):
+                  "oracle_rmsnorm", "oracle_mx4_dequant", "oracle_mx4_untile"):
             getattr(lib, f).restype = ctypes.c_int
         lib.oracle_round_bf16.restype = None
         lib.oracle_param_counts.restype = None
@@ -184,14 +185,37 @@ class Oracle:
         _check(self.lib.oracle_mx4_dequant(rows, n, _p(codes), _p(scales), _p(out)), "oracle_mx4_dequant")
         return out
 
+    def mx4_untile(self, codes, scales):
+        """The tiled byte order of the library's MXFP4 arrays back to row-major.
+        A tile is 16 rows x one 32-element block: codes [..., R/16, n/32, 16, 16]
+        hold, per tile, row r's 16 bytes; scales [..., R/16, n/32, 16] row r's
+        scale byte.  Returns codes [..., R, n/2] and scales [..., R, n/32]."""
+        codes = np.asarray(codes, dtype=np.uint8)
+        scales = np.asarray(scales, dtype=np.uint8)
+        if codes.shape[-2:] != (16, 16) or scales.shape[-1] != 16 or codes.shape[:-1] != scales.shape:
+            raise ValueError("mx4_untile: codes [..., R/16, n/32, 16, 16] and scales [..., R/16, n/32, 16]")
+        lead, rb, nb = codes.shape[:-4], codes.shape[-4], codes.shape[-3]
+        rows = int(np.prod(lead, dtype=np.int64)) * rb * 16
+        codes = np.ascontiguousarray(codes)
+        scales = np.ascontiguousarray(scales)
+        c = np.zeros(lead + (rb * 16, nb * 16), np.uint8)
+        s = np.zeros(lead + (rb * 16, nb), np.uint8)
+        _check(self.lib.oracle_mx4_untile(rows, nb * 32, _p(codes), _p(scales), _p(c), _p(s)), "oracle_mx4_untile")
+        return c, s
+
+    def mx4_dequant_tiled(self, codes, scales):
+        """mx4_dequant of arrays in the library's tiled order (see mx4_untile)."""
+        return self.mx4_dequant(*self.mx4_untile(codes, scales))
+
     def mx4_weights(self, w):
-        """A layer's weights with the expert matrices in MXFP4 (keys <name>_q and
-        <name>_s for gate, up, down and, when present, the shared expert's) ->
-        the float32 weights dict that forward() takes (router and bias as given)."""
+        """A layer's weights with the expert matrices in MXFP4, tiled order (keys
+        <name>_q and <name>_s for gate, up, down and, when present, the shared
+        expert's) -> the float32 weights dict that forward() takes (router and
+        bias as given)."""
         out = {"router": w["router"], "bias": w.get("bias")}
         for name in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down"):
             if w.get(name + "_q") is not None:
-                out[name] = self.mx4_dequant(w[name + "_q"], w[name + "_s"])
+                out[name] = self.mx4_dequant_tiled(w[name + "_q"], w[name + "_s"])
         return out
 
     def threads(self) -> int:
@@ -245,6 +269,14 @@ def param_counts(d):
 
 def mx4_dequant(codes, scales):
     return default().mx4_dequant(codes, scales)
+
+
+def mx4_untile(codes, scales):
+    return default().mx4_untile(codes, scales)
+
+
+def mx4_dequant_tiled(codes, scales):
+    return default().mx4_dequant_tiled(codes, scales)
 
 
 def mx4_weights(w):

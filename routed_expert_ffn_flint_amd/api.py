@@ -155,8 +155,10 @@ def flint_moe_forward(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=No
 
 
 def weights_mx4_struct(d: Dims, w: dict) -> WeightsMx4:
-    """MXFP4 expert weights (keys <name>_q codes and <name>_s scales, uint8; see
-    inputs.mx4_quantize) plus the bf16 router and optional bias."""
+    """MXFP4 expert weights in the tiled order of flint_moe_forward_mx4 (keys
+    <name>_q codes [..., rows/16, cols/32, 16, 16] and <name>_s scales [...,
+    rows/16, cols/32, 16], uint8; see inputs.mx4_quantize and inputs.mx4_tile)
+    plus the bf16 router and optional bias."""
     E, H, I, Is = d.n_experts, d.hidden, d.inter, d.shared_inter
     _check_tensor("router", w["router"], torch.bfloat16, (E, H))
     _check_tensor("router_bias", w.get("bias"), torch.float32, (E,))
@@ -165,8 +167,9 @@ def weights_mx4_struct(d: Dims, w: dict) -> WeightsMx4:
         shapes.update({"shared_gate": (Is, H), "shared_up": (Is, H), "shared_down": (H, Is)})
     ptrs = {}
     for name, shp in shapes.items():
-        _check_tensor(name + "_q", w[name + "_q"], torch.uint8, shp[:-1] + (shp[-1] // 2,))
-        _check_tensor(name + "_s", w[name + "_s"], torch.uint8, shp[:-1] + (shp[-1] // 32,))
+        tiles = shp[:-2] + (shp[-2] // 16, shp[-1] // 32, 16)
+        _check_tensor(name + "_q", w[name + "_q"], torch.uint8, tiles + (16,))
+        _check_tensor(name + "_s", w[name + "_s"], torch.uint8, tiles)
         ptrs[name + "_q"], ptrs[name + "_s"] = _ptr(w[name + "_q"]), _ptr(w[name + "_s"])
     return WeightsMx4(router=_ptr(w["router"]), router_bias=_ptr(w.get("bias")), **ptrs)
 

@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/flint_moe.h"
@@ -77,8 +78,14 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     const size_t TK = (size_t)T * K;
     const int ntiles = (T + kTopkTile - 1) / kTopkTile;
     const ExpertTiles tiles = expert_tiles_for(T, H, E, K, I, Is, eb == 2);
-    const int cap1 = list_capacity(T, K, E, tiles.bm1);
-    const int cap2 = list_capacity(T, K, E, tiles.bm2);
+    int bm1 = tiles.bm1, bm2 = tiles.bm2;
+    if (eb == 2 && T <= kMx4MaxT) {
+        // room for the lists of the MXFP4 kernels too (one workspace size per dims and T)
+        bm1 = std::min(bm1, mx4_bm1());
+        bm2 = std::min(bm2, mx4_bm2());
+    }
+    const int cap1 = list_capacity(T, K, E, bm1);
+    const int cap2 = list_capacity(T, K, E, bm2);
     size_t off = 0;
     char *b = (char *)base;
     auto take = [&](size_t bytes) -> void * {
@@ -259,6 +266,10 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
         return FLINT_DEVICE_ERROR;
 
     DispatchArgs a = dispatch_args(d, T, w);
+    if (e.mx4) {
+        a.bm1 = mx4_bm1();
+        a.bm2 = mx4_bm2();
+    }
     a.logits = w.logits;
     a.logit_splits = router_splits(T, d->hidden, bf16);
     a.topk_idx = topk_idx_out ? topk_idx_out : w.topk_idx;
@@ -351,10 +362,6 @@ flint_status flint_moe_forward_mx4(const flint_moe_dims *d, int32_t T, const voi
     if (st != FLINT_OK) return st;
     if (d->dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
     if (T > kMx4MaxT || !mx4_eligible(T, d->hidden, d->inter, d->shared_inter)) return FLINT_UNSUPPORTED;
-    // the kernels use the workspace's tile lists with their own row tiles
-    const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
-                                               true);
-    if (tiles.bm1 != mx4_bm() || tiles.bm2 != mx4_bm()) return FLINT_UNSUPPORTED;
     st = check_forward(d, T, x, wt ? wt->router : nullptr, wt ? wt->router_bias : nullptr, out, out_dtype,
                        topk_idx_out, topk_w_out, ws, ws_bytes);
     if (st != FLINT_OK || T == 0) return st;

@@ -149,10 +149,12 @@ int stream_bm2();
 hipError_t launch_experts_stream(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 
 // Streaming kernels for MXFP4 expert weights (small batches, bf16 activations):
-// eligibility, rows per tile (both lists), launch of the gate/up and down stages.
+// eligibility, rows per gate/up and per down tile (the dispatch builds its tile
+// lists with these), launch of the gate/up and down stages.
 constexpr int kMx4MaxT = 512;
 bool mx4_eligible(int T, int H, int I, int Is);
-int mx4_bm();
+int mx4_bm1();
+int mx4_bm2();
 hipError_t launch_experts_mx4(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 
 // LDS-tiled kernels for large bf16 batches: rows per gate/up and per down tile

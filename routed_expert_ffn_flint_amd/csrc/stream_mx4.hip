@@ -7,15 +7,21 @@
 // Weight format (a definition; the pages' low-bit builds store 4-bit weights,
 // release news, "Availability"): OCP Microscaling MXFP4 -- FP4 E2M1 elements,
 // 32-element blocks along the reduction dimension, an E8M0 scale 2^(s-127) per
-// block, two elements per byte with the lower-indexed one in the low nibble.
+// block, two elements per byte with the lower-indexed one in the low nibble --
+// stored in tiles of 16 rows x one block: a tile's codes are its 16 rows' 16
+// bytes back to back (256 B), its scales 16 bytes; tiles run along the
+// reduction dimension, then down the rows.
 //
 // Same structure as the bf16 streaming kernels (persistent grid, tile list in
 // LDS, four waves splitting the reduction dimension, ping-pong buffers, partial
 // sums added in wave order), with the weight side 4-bit:
-//   - a step covers CK values of k per wave; lane group g (lane >> 4) takes
-//     elements [k0 + g*CK/4, +CK/4) of its row, which lie in one 32-element
-//     block: CK/8 bytes of codes and one scale byte per weight row, loaded as
-//     one vector and one byte;
+//   - a step covers CK values of k per wave; lane l = row + 16*g takes
+//     elements [k0 + g*CK/4, +CK/4) of its row, which lie in one block: CK/8
+//     code bytes and one scale byte per weight row.  With the tiled storage
+//     the 64 lanes' code bytes are one contiguous stretch (1 KB for CK=128) and
+//     their scale bytes another, so every load is fully coalesced (row-major
+//     storage puts each lane on another row and costs the address unit about
+//     four times as many cache accesses per load);
 //   - the activations use the same assignment of k to lanes, so MFMA j of the
 //     step multiplies elements k0 + g*CK/4 + 8j .. +7 on both sides (the k
 //     order of the sum is permuted, its value is not);
@@ -25,13 +31,36 @@
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
+#ifndef FLINT_MX_MB1
+#define FLINT_MX_MB1 1  // gate/up items: MB1 blocks of 16 rows
+#endif
+#ifndef FLINT_MX_MB2
+#define FLINT_MX_MB2 1  // down items
+#endif
+#ifndef FLINT_MX_NB1
+#define FLINT_MX_NB1 4  // gate/up items: NB1/2 blocks of 16 channels (gate and up each)
+#endif
+#ifndef FLINT_MX_NB2
+#define FLINT_MX_NB2 4  // down items: NB2 blocks of 16 output columns
+#endif
+#ifndef FLINT_MX_CK1
+#define FLINT_MX_CK1 128  // gate/up: k per wave and step
+#endif
+#ifndef FLINT_MX_CK2
+#define FLINT_MX_CK2 64  // down
+#endif
+#ifndef FLINT_MX_GRID_ALL
+#define FLINT_MX_GRID_ALL 0  // one work-group per item instead of a persistent grid
+#endif
+#ifndef FLINT_MX_WGS
+#define FLINT_MX_WGS 2  // work-groups per CU (grid and occupancy)
+#endif
+
 namespace flint {
 
 namespace {
 
 constexpr int kWavesMx = 4;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // E8M0 scale byte -> float (2^(s-127); 0 is the denormal 2^-127, 255 NaN).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
@@ -51,49 +80,90 @@ __device__ __forceinline__ void fp4x8_to_frag(uint32_t codes, float sc, Frag<BF1
 }
 
 // Codes of one step for one weight row: CK/8 bytes (8 or 16).
-template <int CK> struct CodeVec;
-template <> struct CodeVec<64> {
-    uint32_t w[2];
+template <int CK> struct CodeVec {
+    static constexpr int W = CK / 32;  // dwords
+    uint32_t w[W];
     __device__ __forceinline__ void load(const uint8_t *p)
     {
-        const uint2 v = *reinterpret_cast<const uint2 *>(p);
-        w[0] = v.x;
-        w[1] = v.y;
-    }
-};
-template <> struct CodeVec<128> {
-    uint32_t w[4];
-    __device__ __forceinline__ void load(const uint8_t *p)
-    {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
-        w[0] = v[0];
-        w[1] = v[1];
-        w[2] = v[2];
-        w[3] = v[3];
+        if constexpr (W == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+            w[0] = v[0];
+            w[1] = v[1];
+            w[2] = v[2];
+            w[3] = v[3];
+        }
     }
 };
 
-// What one wave needs for one work item.
-template <int MB, int NB>
+// What one wave needs for one work item.  Pointers and strides are the same
+// for every lane (kept in scalar registers); each lane adds its own 32-bit
+// offset, so an item costs a few vector registers whatever NB is.
+template <int MB>
 struct MxItem {
-    const uint16_t *a[MB];  // activation rows, at this lane's k offset
-    const uint8_t *q[NB];   // weight code rows, at this lane's k offset
-    const uint8_t *s[NB];   // weight scale rows, at this lane's block
-    int nstep;              // steps of this wave
+    const uint8_t *qa, *qb;  // codes of the tile row holding row n0: gate (or down), up
+    const uint8_t *sa, *sb;  // scales likewise
+    const uint16_t *abase;   // activations (x, h_sorted or h_shared)
+    uint32_t qrow, srow;     // bytes per tile row (16 weight rows): codes, scales
+    uint32_t qoff, soff;     // this lane's row (lane & 15) and first k within a tile row, in bytes
+    uint32_t aoff[MB];       // this lane's activation row and first k, in elements
+    int nstep;               // steps of this wave
     int row0, row_end, n0, shared, valid;
 };
+
+// Work-group barrier that waits for this wave's LDS accesses only: global
+// loads in flight (the next item's first step) stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The four waves' partial sums added in wave order; every wave gets the total.
+template <int MB, int NB>
+__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[MB][NB], float *red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    f32x4 *r4 = reinterpret_cast<f32x4 *>(red);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) r4[((wave * MB + m) * NB + n) * 64 + lane] = acc[m][n];
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            f32x4 t = r4[(m * NB + n) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < kWavesMx; ++w) {
+                const f32x4 v = r4[((w * MB + m) * NB + n) * 64 + lane];
+                t[0] += v[0];
+                t[1] += v[1];
+                t[2] += v[2];
+                t[3] += v[3];
+            }
+            acc[m][n] = t;
+        }
+}
 
 }  // namespace
 
 // GATE_UP: gate/up + SwiGLU -> h (bf16);  otherwise: down -> y (float32).
 // MB row blocks of 16, NB column blocks of 16 (gate/up: NB/2 gate + NB/2 up).
 template <int MB, int NB, int CK, bool GATE_UP>
-__global__ __launch_bounds__(256, 2) void k_expert_stream_mx4(ExpertArgs a, int n_shared_items)
+__global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertArgs a, int n_shared_items)
 {
     constexpr int BM = MB * 16;
     constexpr int HALF = NB / 2;
     constexpr int BN = GATE_UP ? HALF * 16 : NB * 16;
     constexpr int NF = CK / 32;  // fragments (MFMA k-steps) per step
+    static_assert(CK == 64 || CK == 128, "a lane's slice (CK/4 elements) lies in one 32-element block");
     extern __shared__ int32_t dyn_lds[];
     __shared__ float red[kWavesMx * MB * NB * 256];
 
@@ -103,67 +173,70 @@ __global__ __launch_bounds__(256, 2) void k_expert_stream_mx4(ExpertArgs a, int 
     const int nlist = GATE_UP ? a.meta[0] : a.meta[1];
     int32_t *list = dyn_lds;
     int32_t *offsets = dyn_lds + 2 * nlist;
+    int32_t *toks = offsets + a.E + 1;  // expert-sorted token list (gate/up)
     for (int i = threadIdx.x; i < 2 * nlist; i += blockDim.x) list[i] = (GATE_UP ? a.list1 : a.list2)[i];
     for (int i = threadIdx.x; i <= a.E; i += blockDim.x) offsets[i] = a.offsets[i];
+    if (GATE_UP)
+        for (int i = threadIdx.x; i < a.T * a.K; i += blockDim.x) toks[i] = a.sorted_token[i];
     __syncthreads();
 
-    const int ntn_shared = GATE_UP ? a.Is / BN : (H + BN - 1) / BN;
-    const int ntn_routed = GATE_UP ? a.I / BN : (H + BN - 1) / BN;
+    const int ntn_shared = GATE_UP ? a.Is / BN : H / BN;
+    const int ntn_routed = GATE_UP ? a.I / BN : H / BN;
     const int n_items = n_shared_items + nlist * ntn_routed;
 
     auto get = [&](int item) {
-        MxItem<MB, NB> it;
+        MxItem<MB> it;
         it.valid = item < n_items;
         if (!it.valid) item = 0;  // a valid item's addresses, used only as dummy prefetch targets
-        int e = 0, nt, kdim;
-        const uint8_t *qa, *qb, *sa, *sb;  // codes / scales: gate, up (GATE_UP) or down (qa, sa)
+        int nt, kdim, wrows;
         if (item < n_shared_items) {
             it.shared = 1;
             it.row0 = (item / ntn_shared) * BM;
             nt = item % ntn_shared;
             it.row_end = a.T;
             kdim = GATE_UP ? H : a.Is;
-            qa = (const uint8_t *)(GATE_UP ? a.shared_gate : a.shared_down);
-            sa = GATE_UP ? a.shared_gate_s : a.shared_down_s;
-            qb = (const uint8_t *)a.shared_up;
-            sb = a.shared_up_s;
+            wrows = 0;
+            it.qa = (const uint8_t *)(GATE_UP ? a.shared_gate : a.shared_down);
+            it.sa = GATE_UP ? a.shared_gate_s : a.shared_down_s;
+            it.qb = (const uint8_t *)a.shared_up;
+            it.sb = a.shared_up_s;
         } else {
             it.shared = 0;
             const int r = item - n_shared_items;
             const int entry = r / ntn_routed;
             nt = r % ntn_routed;
-            e = list[2 * entry];
-            it.row0 = list[2 * entry + 1];
-            it.row_end = offsets[e + 1];
+            // list entries and offsets are the same in every lane
+            const int e = __builtin_amdgcn_readfirstlane(list[2 * entry]);
+            it.row0 = __builtin_amdgcn_readfirstlane(list[2 * entry + 1]);
+            it.row_end = __builtin_amdgcn_readfirstlane(offsets[e + 1]);
             kdim = GATE_UP ? H : a.I;
-            const size_t rows_before = (size_t)e * (GATE_UP ? a.I : H);  // weight rows of earlier experts
-            qa = (const uint8_t *)(GATE_UP ? a.gate : a.down) + rows_before * (kdim / 2);
-            sa = (GATE_UP ? a.gate_s : a.down_s) + rows_before * (kdim / 32);
-            qb = (const uint8_t *)a.up + rows_before * (kdim / 2);
-            sb = a.up_s + rows_before * (kdim / 32);
+            wrows = e * (GATE_UP ? a.I : H);  // weight rows of earlier experts
+            it.qa = (const uint8_t *)(GATE_UP ? a.gate : a.down);
+            it.sa = GATE_UP ? a.gate_s : a.down_s;
+            it.qb = (const uint8_t *)a.up;
+            it.sb = a.up_s;
         }
         it.n0 = nt * BN;
+        it.qrow = kdim * 8;   // kdim/32 tiles of 256 code bytes
+        it.srow = kdim / 2;   // kdim/32 tiles of 16 scale bytes
+        const size_t first_tile_row = ((size_t)wrows + it.n0) / 16;
+        it.qa += first_tile_row * it.qrow;
+        it.qb += first_tile_row * it.qrow;
+        it.sa += first_tile_row * it.srow;
+        it.sb += first_tile_row * it.srow;
         it.nstep = kdim / CK / kWavesMx;  // the launcher checks divisibility (and evenness)
         const int kw = wave * it.nstep * CK + g * (CK / 4);  // this lane's first k
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-            int c = GATE_UP ? it.n0 + (n % HALF) * 16 + (lane & 15) : it.n0 + n * 16 + (lane & 15);
-            if (!GATE_UP && c >= H) c = 0;
-            const bool up = GATE_UP && n >= HALF;
-            it.q[n] = (up ? qb : qa) + (size_t)c * (kdim / 2) + kw / 2;
-            it.s[n] = (up ? sb : sa) + (size_t)c * (kdim / 32) + kw / 32;
-        }
+        // tile kw/32, the lane's row within it, the byte of element kw in that row
+        it.qoff = (kw / 32) * 256 + (lane & 15) * 16 + (kw % 32) / 2;
+        it.soff = (kw / 32) * 16 + (lane & 15);
+        it.abase = GATE_UP ? (const uint16_t *)a.x
+                           : (it.shared ? (const uint16_t *)a.h_shared : (const uint16_t *)a.h_sorted);
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             int r = it.row0 + m * 16 + (lane & 15);
             if (r >= it.row_end) r = it.row0;  // rows past the tile repeat its first row (cache hits)
-            if (GATE_UP) {
-                const int tok = it.shared ? r : a.sorted_token[r];
-                it.a[m] = (const uint16_t *)a.x + (size_t)tok * H + kw;
-            } else {
-                it.a[m] = (it.shared ? (const uint16_t *)a.h_shared : (const uint16_t *)a.h_sorted) +
-                          (size_t)r * kdim + kw;
-            }
+            const int arow = GATE_UP ? (it.shared ? r : toks[r]) : r;
+            it.aoff[m] = (uint32_t)arow * (GATE_UP ? H : kdim) + kw;
         }
         return it;
     };
@@ -174,39 +247,54 @@ __global__ __launch_bounds__(256, 2) void k_expert_stream_mx4(ExpertArgs a, int 
         CodeVec<CK> q[NB];
         uint32_t s[NB];
     };
-    auto load = [&](const MxItem<MB, NB> &it, int step, Raw &r) {
+    auto load = [&](const MxItem<MB> &it, int step, Raw &r) {
+        // a step advances CK/32 tiles; with lane l = row + 16 * group, the lanes
+        // of one load read one contiguous stretch of codes (CK * 8 bytes)
+        const uint32_t qo = it.qoff + step * (CK * 8), so = it.soff + step * (CK / 2);
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-            r.q[n].load(it.q[n] + step * (CK / 2));
-            r.s[n] = it.s[n][step * (CK / 32)];
+            const bool up = GATE_UP && n >= HALF;
+            const uint32_t trow = (uint32_t)(GATE_UP ? n % HALF : n);  // tile rows past the first
+            r.q[n].load((up ? it.qb : it.qa) + trow * it.qrow + qo);
+            r.s[n] = (up ? it.sb : it.sa)[trow * it.srow + so];
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
-            for (int j = 0; j < NF; ++j) r.fa[m][j].load(it.a[m] + step * CK + 8 * j);
+            for (int j = 0; j < NF; ++j) r.fa[m][j].load(it.abase + (it.aoff[m] + step * CK + 8 * j));
     };
     f32x4 acc[MB][NB];
     auto compute = [&](const Raw &r) {
+        float sc[NB];
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-            const float sc = e8m0_to_f32(r.s[n]);
+            // the empty asm pins the scale decode here: without it the compiler
+            // hoists the decode's compares to just after the scale load is
+            // issued, and the wave then waits on that load a phase early
+            uint32_t sv = r.s[n];
+            asm volatile("" : "+v"(sv));
+            sc[n] = e8m0_to_f32(sv);
+        }
+        // k-slice outer, columns inner: consecutive MFMAs use different
+        // accumulators, so none waits for the previous one's result
 #pragma unroll
-            for (int j = 0; j < NF; ++j) {
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
                 Frag<BF16> fb;
-                fp4x8_to_frag(r.q[n].w[j], sc, fb);
+                fp4x8_to_frag(r.q[n].w[j], sc[n], fb);
 #pragma unroll
                 for (int m = 0; m < MB; ++m) mma(acc[m][n], r.fa[m][j], fb);
             }
-        }
     };
 
     int item = blockIdx.x;
-    MxItem<MB, NB> cur = get(item);
+    MxItem<MB> cur = get(item);
     if (!cur.valid) return;  // uniform across the work-group
     Raw ra, rb;
     load(cur, 0, ra);
     while (true) {
-        const MxItem<MB, NB> nxt = get(item + gridDim.x);
+        const MxItem<MB> nxt = get(item + gridDim.x);
         zero_acc(acc);
         for (int st = 0; st < cur.nstep; st += 2) {
             // scheduling barriers keep each phase in program order, so that a
@@ -224,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_stream_mx4(ExpertArgs a, int 
             compute(rb);
             __builtin_amdgcn_sched_barrier(0);
         }
-        splitk_reduce<kWavesMx, MB, NB>(acc, red);
+        reduce_waves<MB, NB>(acc, red);
         if (GATE_UP) {
             uint16_t *hout = cur.shared ? (uint16_t *)a.h_shared : (uint16_t *)a.h_sorted;
             const int width = cur.shared ? a.Is : a.I;
@@ -247,7 +335,6 @@ __global__ __launch_bounds__(256, 2) void k_expert_stream_mx4(ExpertArgs a, int 
             for (int n = 0; n < NB; ++n) {
                 if ((n % kWavesMx) != wave) continue;
                 const int c = cur.n0 + n * 16 + (lane & 15);
-                if (c >= H) continue;
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -257,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_stream_mx4(ExpertArgs a, int 
                     }
             }
         }
-        __syncthreads();  // every wave has read `red` before the next item overwrites it
+        lds_barrier();  // every wave has read `red` before the next item overwrites it
         if (!nxt.valid) break;
         cur = nxt;
         item += gridDim.x;
@@ -265,35 +352,39 @@ __global__ __launch_bounds__(256, 2) void k_expert_stream_mx4(ExpertArgs a, int 
 }
 
 namespace {
-constexpr int kMxMB = 2, kMxNB1 = 4, kMxNB2 = 2, kMxCK1 = 128, kMxCK2 = 64;
-}
+constexpr int kMxMB1 = FLINT_MX_MB1, kMxMB2 = FLINT_MX_MB2;
+constexpr int kMxNB1 = FLINT_MX_NB1, kMxNB2 = FLINT_MX_NB2;
+constexpr int kMxCK1 = FLINT_MX_CK1, kMxCK2 = FLINT_MX_CK2;
+}  // namespace
 
 bool mx4_eligible(int T, int H, int I, int Is)
 {
-    // every item's reduction splits into 4 waves x an even number of steps
+    // every item's reduction splits into 4 waves x an even number of steps,
+    // and every column tile is whole
     return T <= kMx4MaxT && H % (kWavesMx * 2 * kMxCK1) == 0 && I % (kWavesMx * 2 * kMxCK2) == 0 &&
-           Is % (kWavesMx * 2 * kMxCK2) == 0 && I % (kMxNB1 / 2 * 16) == 0 && Is % (kMxNB1 / 2 * 16) == 0;
+           Is % (kWavesMx * 2 * kMxCK2) == 0 && I % (kMxNB1 / 2 * 16) == 0 && Is % (kMxNB1 / 2 * 16) == 0 &&
+           H % (kMxNB2 * 16) == 0;
 }
 
-int mx4_bm() { return kMxMB * 16; }
+int mx4_bm1() { return kMxMB1 * 16; }
+int mx4_bm2() { return kMxMB2 * 16; }
 
 hipError_t launch_experts_mx4(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
-    const int bm = kMxMB * 16;
+    const int bm1 = kMxMB1 * 16, bm2 = kMxMB2 * 16;
     const int bn1 = kMxNB1 / 2 * 16, bn2 = kMxNB2 * 16;
-    const int cap = list_capacity(a.T, a.K, a.E, bm);
-    const int mt = (a.T + bm - 1) / bm;
-    const int ns1 = a.Is > 0 ? mt * (a.Is / bn1) : 0;
-    const int ns2 = a.Is > 0 ? mt * ((a.H + bn2 - 1) / bn2) : 0;
-    const int max1 = ns1 + cap * (a.I / bn1);
-    const int max2 = ns2 + cap * ((a.H + bn2 - 1) / bn2);
-    const size_t lds = (size_t)(2 * cap + a.E + 1) * 4;
-    const int grid_cap = 2 * max(a.cus, 1);
-    hipError_t err = launch_k(k_expert_stream_mx4<kMxMB, kMxNB1, kMxCK1, true>, min(grid_cap, max1), 256, lds, stream,
-                              marks ? marks[0] : Marks{}, a, ns1);
+    const int cap1 = list_capacity(a.T, a.K, a.E, bm1), cap2 = list_capacity(a.T, a.K, a.E, bm2);
+    const int ns1 = a.Is > 0 ? (a.T + bm1 - 1) / bm1 * (a.Is / bn1) : 0;
+    const int ns2 = a.Is > 0 ? (a.T + bm2 - 1) / bm2 * (a.H / bn2) : 0;
+    const int max1 = ns1 + cap1 * (a.I / bn1);
+    const int max2 = ns2 + cap2 * (a.H / bn2);
+    const int grid_cap = FLINT_MX_GRID_ALL ? (1 << 30) : FLINT_MX_WGS * max(a.cus, 1);
+    hipError_t err = launch_k(k_expert_stream_mx4<kMxMB1, kMxNB1, kMxCK1, true>, min(grid_cap, max1), 256,
+                              (size_t)(2 * cap1 + a.E + 1 + a.T * a.K) * 4, stream, marks ? marks[0] : Marks{}, a,
+                              ns1);
     if (err != hipSuccess) return err;
-    return launch_k(k_expert_stream_mx4<kMxMB, kMxNB2, kMxCK2, false>, min(grid_cap, max2), 256, lds, stream,
-                    marks ? marks[1] : Marks{}, a, ns2);
+    return launch_k(k_expert_stream_mx4<kMxMB2, kMxNB2, kMxCK2, false>, min(grid_cap, max2), 256,
+                    (size_t)(2 * cap2 + a.E + 1) * 4, stream, marks ? marks[1] : Marks{}, a, ns2);
 }
 
 }  // namespace flint

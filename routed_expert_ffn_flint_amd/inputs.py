@@ -13,7 +13,7 @@ here, so every tensor is drawn):
   skew16384    T=16384, same layer, Zipf(1.1) per-expert router bias, seed 0
   stack47      T=256,   47 distinct layers, RMSNorm between layers,   seed 1
   decode32_mx4 decode32 with every expert matrix stored as MXFP4 (block-scaled
-               4-bit, see mx4_quantize); router bf16
+               4-bit, see mx4_quantize, in the tiled order of mx4_tile); router bf16
 
 Weights ~ N(0, 0.02^2), hidden states ~ N(0, 1), drawn in float32 and rounded
 to bf16 (round-to-nearest-even, torch's conversion) for the bf16 workloads.
@@ -147,6 +147,20 @@ def mx4_quantize(w: torch.Tensor):
     return codes, scales
 
 
+def mx4_tile(codes: torch.Tensor, scales: torch.Tensor):
+    """Row-major MXFP4 arrays (codes [..., R, n/2], scales [..., R, n/32], as
+    mx4_quantize returns them) in the tiled byte order the kernels read: a tile
+    is 16 rows x one 32-element block; codes [..., R/16, n/32, 16, 16] (per
+    tile, each row's 16 bytes, rows in order), scales [..., R/16, n/32, 16]."""
+    R, nb = codes.shape[-2], scales.shape[-1]
+    if R % 16:
+        raise ValueError("mx4_tile: the row count must be a multiple of 16")
+    lead = tuple(codes.shape[:-2])
+    c = codes.reshape(lead + (R // 16, 16, nb, 16)).transpose(-3, -2).contiguous()
+    s = scales.reshape(lead + (R // 16, 16, nb)).transpose(-2, -1).contiguous()
+    return c, s
+
+
 def make_layer(wl: Workload, layer: int = 0, device="cpu", with_shared: bool = True) -> dict:
     """Weights of one layer as torch tensors on ``device``.
 
@@ -170,10 +184,10 @@ def make_layer(wl: Workload, layer: int = 0, device="cpu", with_shared: bool = T
         w["shared_up"] = _normal((Is, H), WEIGHT_STD, dt, s, layer, "shared_up", device)
         w["shared_down"] = _normal((H, Is), WEIGHT_STD, dt, s, layer, "shared_down", device)
     if wl.mx4:
-        # stored as MXFP4: <name>_q codes and <name>_s scales replace <name>
+        # stored as MXFP4 in tiled order: <name>_q codes and <name>_s scales replace <name>
         for name in EXPERT_MATRICES:
             if name in w:
-                w[name + "_q"], w[name + "_s"] = mx4_quantize(w.pop(name))
+                w[name + "_q"], w[name + "_s"] = mx4_tile(*mx4_quantize(w.pop(name)))
     return w
 
 

@@ -53,24 +53,25 @@ def host_weights(w: dict, experts=None) -> dict:
 
 
 def host_weights_mx4(w: dict, experts=None) -> dict:
-    """MXFP4 weights (codes and scales on the device) decoded by the oracle into
-    float32 host arrays; with ``experts`` given, only those experts' matrices
-    (the rest stay zero), as in host_weights."""
+    """MXFP4 weights (tiled codes and scales on the device) decoded by the oracle
+    into float32 host arrays; with ``experts`` given, only those experts'
+    matrices (the rest stay zero), as in host_weights."""
     out = {"router": inputs.to_numpy_f32(w["router"]), "bias": inputs.to_numpy_f32(w.get("bias"))}
     for k in ("shared_gate", "shared_up", "shared_down"):
         if w.get(k + "_q") is not None:
-            out[k] = orc.mx4_dequant(w[k + "_q"].cpu().numpy(), w[k + "_s"].cpu().numpy())
+            out[k] = orc.mx4_dequant_tiled(w[k + "_q"].cpu().numpy(), w[k + "_s"].cpu().numpy())
     for k in ("gate", "up", "down"):
         q, sc = w[k + "_q"], w[k + "_s"]
-        shape = tuple(q.shape[:-1]) + (q.shape[-1] * 2,)
+        E, RB, KB = q.shape[:3]
+        shape = (E, RB * 16, KB * 32)
         if experts is None:
-            out[k] = orc.mx4_dequant(q.cpu().numpy(), sc.cpu().numpy())
+            out[k] = orc.mx4_dequant_tiled(q.cpu().numpy(), sc.cpu().numpy())
         else:
             full = np.zeros(shape, np.float32)
             ex = torch.as_tensor(np.asarray(sorted(experts)), device=q.device, dtype=torch.long)
             if len(ex):
-                full[ex.cpu().numpy()] = orc.mx4_dequant(q.index_select(0, ex).cpu().numpy(),
-                                                          sc.index_select(0, ex).cpu().numpy())
+                full[ex.cpu().numpy()] = orc.mx4_dequant_tiled(q.index_select(0, ex).cpu().numpy(),
+                                                                sc.index_select(0, ex).cpu().numpy())
             out[k] = full
     return out
 

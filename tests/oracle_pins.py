@@ -402,8 +402,38 @@ def pin_mx4_layout(orc):
     assert packed[0, 0] == 0x10  # hand check of the packing: elements 0 (code 0) and 1 (code 1)
 
 
+def pin_mx4_tiled_layout(orc):
+    # A 32 x 64 matrix is 2 x 2 tiles (16 rows x 32 elements each), stored tile
+    # (0,0), (0,1), (1,0), (1,1); a tile holds 16 rows of 16 code bytes, then the
+    # next tile.  Hand-placed markers and where the definition puts them:
+    #   code byte 0    tile 0, row 0,  byte 0   -> row 0,  byte 0
+    #   code byte 255  tile 0, row 15, byte 15  -> row 15, byte 15
+    #   code byte 256  tile 1, row 0,  byte 0   -> row 0,  byte 16
+    #   code byte 512  tile 2, row 0,  byte 0   -> row 16, byte 0
+    #   code byte 786  tile 3, row 1,  byte 2   -> row 17, byte 18 (elements 36, 37)
+    #   scale byte 17  tile 1, row 1            -> scales[1][1]
+    #   scale byte 40  tile 2, row 8            -> scales[24][0]
+    codes_t = np.zeros(2 * 2 * 16 * 16, np.uint8)
+    scales_t = np.zeros(2 * 2 * 16, np.uint8)
+    marks = {0: (0, 0), 255: (15, 15), 256: (0, 16), 512: (16, 0), 786: (17, 18)}
+    for i, flat in enumerate(marks):
+        codes_t[flat] = 1 + i
+    scales_t[17], scales_t[40] = 200, 201
+    c, s = orc.mx4_untile(codes_t.reshape(2, 2, 16, 16), scales_t.reshape(2, 2, 16))
+    assert c.shape == (32, 32) and s.shape == (32, 2)
+    for i, (flat, (r, b)) in enumerate(marks.items()):
+        assert c[r, b] == 1 + i, (flat, r, b)
+    assert np.count_nonzero(c) == len(marks)
+    assert s[1, 1] == 200 and s[24, 0] == 201 and np.count_nonzero(s) == 2
+    # stacked matrices: the second one's first tile is row 32's first bytes
+    codes2 = np.zeros((2, 2, 2, 16, 16), np.uint8)
+    codes2[1, 0, 0, 0, 0] = 9
+    c2, _ = orc.mx4_untile(codes2, np.zeros((2, 2, 2, 16), np.uint8))
+    assert c2.shape == (2, 32, 32) and c2[1, 0, 0] == 9 and np.count_nonzero(c2) == 1
+
+
 ALL_PINS = [pin_param_counts, pin_bf16_rounding, pin_routing_hand_top2, pin_routing_hand_all,
             pin_routing_equal_logits, pin_routing_tie_break, pin_routing_limits, pin_routing_bias,
             pin_routing_library, pin_expert_closed_form, pin_bf16_intermediate, pin_dense_mixture,
             pin_shared_split, pin_token_permutation, pin_dispatch_hand, pin_dispatch_invariants,
-            pin_rmsnorm, pin_mx4_element_table, pin_mx4_scale, pin_mx4_layout]
+            pin_rmsnorm, pin_mx4_element_table, pin_mx4_scale, pin_mx4_layout, pin_mx4_tiled_layout]

@@ -64,6 +64,10 @@ MUTANTS = [
     ("mx4_scale_bias_128", "ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
     ("mx4_no_subnormal", "e == 0 ? 0.5 * m", "e == 0 ? 1.0 * m"),
     ("mx4_element_bias_0", "ldexp(1.0 + 0.5 * m, (int)e - 1)", "ldexp(1.0 + 0.5 * m, (int)e)"),
+    ("mx4_untile_tiles_down_first", "const int64_t tile = rb * nkb + kb;",
+     "const int64_t tile = kb * (rows / 16) + rb;"),
+    ("mx4_untile_row_byte_swapped", "codes_t[(tile * 16 + r) * 16 + j]", "codes_t[(tile * 16 + j) * 16 + r]"),
+    ("mx4_untile_scale_rows_reversed", "= scales_t[tile * 16 + r];", "= scales_t[tile * 16 + 15 - r];"),
 ]
 
 
