@@ -20,6 +20,10 @@
 //   k_dispatch_scatter (more than one tile) slot = offset + tile base + rank.
 #include <climits>
 
+#ifndef FLINT_TOPK_WAVE
+#define FLINT_TOPK_WAVE 1  // T <= 1024: bitwise K-th-largest search (1) or sorted-list merges (0)
+#endif
+
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
@@ -362,6 +366,82 @@ __device__ __forceinline__ void write_topk(const uint64_t (&l)[kMaxTopK], int t,
         }
 }
 
+// Top-K of one token by one wave (E <= 256: four candidates per lane, expert
+// lane + 64*i), by a bitwise search for the K-th largest score: float32 scores
+// are >= 0, so their bit patterns order like the values, and the K-th largest
+// pattern is the largest v with at least K patterns >= v, found one bit at a
+// time from the top with wave-wide counts (ballots).  Then every score above
+// it is selected, and of those equal to it the lowest expert indices up to K.
+// A chain of ~32 short compare/count steps instead of log2(64) merges of
+// sorted 8-entry lists.  Writes topk_idx (ascending ids) and topk_w (s over
+// the sum of the K selected, the sum in double in ascending id order).
+__device__ __forceinline__ void wave_topk(const float *zt, size_t split_stride, int nsplit, int E, int K, int t,
+                                          int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+                                          float *ls, int *le)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t u[4];
+    bool v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E;
+        float z = 0.f;
+        if (v[i]) {
+            z = zt[e];
+            for (int sp = 1; sp < nsplit; ++sp) z += zt[sp * split_stride + e];  // partial sums, in order
+        }
+        u[i] = v[i] ? __float_as_uint(score_from_logit(z)) : 0u;
+    }
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(v[i] && u[i] >= cand));
+        if (cnt >= K) thr = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(v[i] && u[i] > thr));
+    const int need = K - gt;  // taken from the scores equal to thr, lowest ids first
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint64_t eq = __ballot(v[i] && u[i] == thr);
+        const int eq_rank = eq_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
+        const bool sel = v[i] && (u[i] > thr || (u[i] == thr && eq_rank < need));
+        const uint64_t sm = __ballot(sel);
+        if (sel) {
+            const int r = sel_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+            ls[r] = __uint_as_float(u[i]);
+            le[r] = lane + 64 * i;
+        }
+        eq_before += __popcll(eq);
+        sel_before += __popcll(sm);
+    }
+    __builtin_amdgcn_wave_barrier();
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) sum += (double)ls[k];
+    if (lane < K) {
+        topk_idx[(size_t)t * K + lane] = le[lane];
+        topk_w[(size_t)t * K + lane] = (float)((double)ls[lane] / sum);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_topk_wave(DispatchArgs da)
+{
+    __shared__ float ls[4][kMaxTopK];
+    __shared__ int le[4][kMaxTopK];
+    const int wave = threadIdx.x >> 6;
+    const int tok = blockIdx.x * 4 + wave;
+    if (tok >= da.T) return;  // whole waves
+    wave_topk(da.logits + (size_t)tok * da.E, (size_t)da.T * da.E, da.logit_splits, da.E, da.K, tok, da.topk_idx,
+              da.topk_w, ls[wave], le[wave]);
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void k_topk(DispatchArgs da)
 {
@@ -440,7 +520,7 @@ hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks
     Marks first{m.start, a.dispatch ? nullptr : m.stop};
     hipError_t err = hipSuccess;
     if (a.compute_topk) {
-        err = a.T <= 1024 ? launch_k(k_topk<64>, (a.T + 3) / 4, 256, 0, stream, first, a)
+        err = a.T <= 1024 ? launch_k(FLINT_TOPK_WAVE ? k_topk_wave : k_topk<64>, (a.T + 3) / 4, 256, 0, stream, first, a)
                           : launch_k(k_topk<16>, (a.T + 15) / 16, 256, 0, stream, first, a);
         if (err != hipSuccess) return err;
         first.start = nullptr;

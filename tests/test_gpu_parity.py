@@ -186,6 +186,38 @@ def test_route_entry_point_matches_forward_routing():
     assert torch.equal(idx, idx2) and torch.equal(tw, tw2)
 
 
+@pytest.mark.parametrize("T", [37, 1500])  # one wave per token (T <= 1024), 16-lane groups above
+def test_route_exact_ties_go_to_the_lower_index(T):
+    """Router rows in groups of four identical rows, group g scaled by (1 + g):
+    the four experts of a group get equal float32 scores on both sides, so with
+    K = 6 the boundary falls inside a group for every token and the selection
+    must take that group's lowest ids.  Distinct groups are far apart except for
+    tokens with x . r0 near 0, which are left out (counted)."""
+    H, E, K = 256, 64, 6
+    g = torch.Generator().manual_seed(11)
+    r0 = torch.randn(H, generator=g) * 0.05
+    router = ((1.0 + (torch.arange(E) // 4).float())[:, None] * r0[None, :]).to(torch.bfloat16)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    wl = inputs.custom("ties", T, H, E, K, 64, 0, True)
+    idx, tw = api.route(api.dims_of(wl), x.cuda(), router.cuda(), None)
+    dd = G.oracle_dims(wl)
+    xh, rh = inputs.to_numpy_f32(x), inputs.to_numpy_f32(router)
+    o_idx, o_w, _ = orc.route(dd, xh, rh, None)
+    sc = orc.scores(dd, xh, rh, None)
+    checked = boundary_ties = 0
+    for t in range(T):
+        vals = np.unique(sc[t])[::-1]  # distinct scores, descending
+        if np.min(vals[:-1] - vals[1:]) < 1e-5:
+            continue  # distinct groups too close to call
+        srt = np.sort(sc[t])[::-1]
+        boundary_ties += int(srt[K - 1] == srt[K])
+        checked += 1
+        assert idx[t].tolist() == o_idx[t].tolist(), (t, idx[t].tolist(), o_idx[t].tolist())
+        np.testing.assert_allclose(tw[t].cpu().numpy(), o_w[t], rtol=0, atol=G.WEIGHT_TOL)
+    print(f"ties T={T}: {checked} tokens checked, {boundary_ties} with a tie at the boundary")
+    assert checked >= T // 2 and boundary_ties == checked
+
+
 @pytest.mark.parametrize("name", ["decode32", "prefill4096"])
 def test_deterministic(name):
     wl = inputs.WORKLOADS[name]
