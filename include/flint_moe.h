@@ -195,7 +195,7 @@ typedef struct {
 /* flint_moe_forward with MXFP4 expert weights.  Same arguments and results as
  * flint_moe_forward otherwise; the workspace is flint_moe_workspace_bytes(dims,
  * T).  Supported: dims.dtype == FLINT_BF16, T <= 512, H a multiple of 1024, I
- * and Is multiples of 512 (Is may be 0), 16-byte aligned code arrays; anything
+ * and Is multiples of 256 (Is may be 0), 16-byte aligned code arrays; anything
  * else is refused with FLINT_UNSUPPORTED.  The weight arrays are read only.  `events` as in
  * flint_moe_forward_profiled (10 handles) or NULL. */
 flint_status flint_moe_forward_mx4(const flint_moe_dims *dims, int32_t T, const void *x,

@@ -248,30 +248,37 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
     const int H = a.H, K = a.K;
     const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
     if (c >= H) return;
+    // Every load is issued before any is used (entries past K re-read entry
+    // K-1, rows past them are not added): the rows arrive in one memory
+    // latency instead of one each.
     int slots[kMaxTopK];
     float w[kMaxTopK];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
-        slots[k] = k < K ? a.slot_of[(size_t)t * K + k] : 0;
-        w[k] = k < K ? a.topk_w[(size_t)t * K + k] : 0.f;
+        const size_t i = (size_t)t * K + (k < K ? k : K - 1);
+        slots[k] = a.slot_of[i];
+        w[k] = a.topk_w[i];
     }
+    f32x4 y[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) y[k] = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
+    const f32x4 ys = a.Is > 0 ? *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
         if (k < K) {
-            const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
-            acc[0] += w[k] * y[0];
-            acc[1] += w[k] * y[1];
-            acc[2] += w[k] * y[2];
-            acc[3] += w[k] * y[3];
+            acc[0] += w[k] * y[k][0];
+            acc[1] += w[k] * y[k][1];
+            acc[2] += w[k] * y[k][2];
+            acc[3] += w[k] * y[k][3];
         }
     }
     if (a.Is > 0) {
-        const f32x4 y = *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c);
-        acc[0] += y[0];
-        acc[1] += y[1];
-        acc[2] += y[2];
-        acc[3] += y[3];
+        acc[0] += ys[0];
+        acc[1] += ys[1];
+        acc[2] += ys[2];
+        acc[3] += ys[3];
     }
     if (a.out_bf16) {
         uint16_t *o = (uint16_t *)a.out + (size_t)t * H + c;

@@ -214,15 +214,18 @@ __device__ __forceinline__ void group_top8(const float *zt, size_t split_stride,
     const int gl = threadIdx.x & (G - 1);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) l[j] = 0;
+    // every load unconditional (experts past E read expert 0 and are masked),
+    // so they go out together instead of one latency each
+    float zs[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) zs[i] = zt[gl + G * i < E ? gl + G * i : 0];
+    for (int sp = 1; sp < nsplit; ++sp)  // partial sums, in order
+#pragma unroll
+        for (int i = 0; i < C; ++i) zs[i] += zt[sp * split_stride + (gl + G * i < E ? gl + G * i : 0)];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int e = gl + G * i;
-        float z = 0.f;
-        if (e < E) {
-            z = zt[e];
-            for (int sp = 1; sp < nsplit; ++sp) z += zt[sp * split_stride + e];  // partial sums, in order
-        }
-        uint64_t k = e < E ? sel_key(score_from_logit(z), e) : 0;
+        uint64_t k = e < E ? sel_key(score_from_logit(zs[i]), e) : 0;
         if (C <= kMaxTopK) {
             l[i] = k;  // fewer candidates than list slots: keep all, sort below
         } else if (k > l[kMaxTopK - 1]) {
@@ -382,17 +385,20 @@ __device__ __forceinline__ void wave_topk(const float *zt, size_t split_stride, 
     const int lane = threadIdx.x & 63;
     uint32_t u[4];
     bool v[4];
+    float z[4];
+    // every load unconditional (experts past E read expert 0 and are masked),
+    // so the four go out together instead of one latency each
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
         v[i] = e < E;
-        float z = 0.f;
-        if (v[i]) {
-            z = zt[e];
-            for (int sp = 1; sp < nsplit; ++sp) z += zt[sp * split_stride + e];  // partial sums, in order
-        }
-        u[i] = v[i] ? __float_as_uint(score_from_logit(z)) : 0u;
+        z[i] = zt[v[i] ? e : 0];
     }
+    for (int sp = 1; sp < nsplit; ++sp)  // partial sums, in order
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] += zt[sp * split_stride + (v[i] ? lane + 64 * i : 0)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = v[i] ? __float_as_uint(score_from_logit(z[i])) : 0u;
     uint32_t thr = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = thr | (1u << bit);

@@ -13,8 +13,10 @@
 // reduction dimension, then down the rows.
 //
 // Same structure as the bf16 streaming kernels (persistent grid, tile list in
-// LDS, four waves splitting the reduction dimension, ping-pong buffers, partial
-// sums added in wave order), with the weight side 4-bit:
+// LDS, ping-pong register buffers; gate/up items shared by four waves that
+// split the reduction dimension and add their partial sums in wave order),
+// except that a down item (a reduction of only I) belongs to one wave, which
+// needs neither LDS sums nor barriers; the weight side is 4-bit:
 //   - a step covers CK values of k per wave; lane l = row + 16*g takes
 //     elements [k0 + g*CK/4, +CK/4) of its row, which lie in one block: CK/8
 //     code bytes and one scale byte per weight row.  With the tiled storage
@@ -47,7 +49,13 @@
 #define FLINT_MX_CK1 128  // gate/up: k per wave and step
 #endif
 #ifndef FLINT_MX_CK2
-#define FLINT_MX_CK2 64  // down
+#define FLINT_MX_CK2 128  // down
+#endif
+#ifndef FLINT_MX_KS1
+#define FLINT_MX_KS1 4  // gate/up: waves sharing an item (4: split reduction; 1: a wave per item)
+#endif
+#ifndef FLINT_MX_KS2
+#define FLINT_MX_KS2 1  // down
 #endif
 #ifndef FLINT_MX_GRID_ALL
 #define FLINT_MX_GRID_ALL 0  // one work-group per item instead of a persistent grid
@@ -156,7 +164,10 @@ __device__ __forceinline__ void reduce_waves(f32x4 (&acc)[MB][NB], float *red)
 
 // GATE_UP: gate/up + SwiGLU -> h (bf16);  otherwise: down -> y (float32).
 // MB row blocks of 16, NB column blocks of 16 (gate/up: NB/2 gate + NB/2 up).
-template <int MB, int NB, int CK, bool GATE_UP>
+// KSPLIT 4: the four waves of a work-group share each item, a quarter of the
+// reduction each, and add their partial sums in LDS; KSPLIT 1: every wave
+// walks its own items over the whole reduction (no LDS sums, no barriers).
+template <int MB, int NB, int CK, bool GATE_UP, int KSPLIT>
 __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertArgs a, int n_shared_items)
 {
     constexpr int BM = MB * 16;
@@ -165,7 +176,8 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
     constexpr int NF = CK / 32;  // fragments (MFMA k-steps) per step
     static_assert(CK == 64 || CK == 128, "a lane's slice (CK/4 elements) lies in one 32-element block");
     extern __shared__ int32_t dyn_lds[];
-    __shared__ float red[kWavesMx * MB * NB * 256];
+    static_assert(KSPLIT == 1 || KSPLIT == kWavesMx, "waves per item");
+    __shared__ float red[KSPLIT > 1 ? kWavesMx * MB * NB * 256 : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4;
@@ -224,8 +236,8 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
         it.qb += first_tile_row * it.qrow;
         it.sa += first_tile_row * it.srow;
         it.sb += first_tile_row * it.srow;
-        it.nstep = kdim / CK / kWavesMx;  // the launcher checks divisibility (and evenness)
-        const int kw = wave * it.nstep * CK + g * (CK / 4);  // this lane's first k
+        it.nstep = kdim / CK / KSPLIT;  // the launcher checks divisibility (and evenness)
+        const int kw = (KSPLIT > 1 ? wave * it.nstep * CK : 0) + g * (CK / 4);  // this lane's first k
         // tile kw/32, the lane's row within it, the byte of element kw in that row
         it.qoff = (kw / 32) * 256 + (lane & 15) * 16 + (kw % 32) / 2;
         it.soff = (kw / 32) * 16 + (lane & 15);
@@ -288,13 +300,16 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
             }
     };
 
-    int item = blockIdx.x;
+    // KSPLIT 4: work-group b takes items b, b + grid, ...; KSPLIT 1: wave w of
+    // work-group b takes items 4b + w, 4b + w + 4 grid, ...
+    int item = KSPLIT > 1 ? blockIdx.x : blockIdx.x * kWavesMx + wave;
+    const int stride = KSPLIT > 1 ? gridDim.x : gridDim.x * kWavesMx;
     MxItem<MB> cur = get(item);
-    if (!cur.valid) return;  // uniform across the work-group
+    if (!cur.valid) return;  // uniform across the work-group (KSPLIT 4) or the wave (1)
     Raw ra, rb;
     load(cur, 0, ra);
     while (true) {
-        const MxItem<MB> nxt = get(item + gridDim.x);
+        const MxItem<MB> nxt = get(item + stride);
         zero_acc(acc);
         for (int st = 0; st < cur.nstep; st += 2) {
             // scheduling barriers keep each phase in program order, so that a
@@ -312,13 +327,13 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
             compute(rb);
             __builtin_amdgcn_sched_barrier(0);
         }
-        reduce_waves<MB, NB>(acc, red);
+        if (KSPLIT > 1) reduce_waves<MB, NB>(acc, red);
         if (GATE_UP) {
             uint16_t *hout = cur.shared ? (uint16_t *)a.h_shared : (uint16_t *)a.h_sorted;
             const int width = cur.shared ? a.Is : a.I;
 #pragma unroll
             for (int j = 0; j < HALF; ++j) {
-                if ((j % kWavesMx) != wave) continue;
+                if (KSPLIT > 1 && (j % kWavesMx) != wave) continue;
                 const int c = cur.n0 + j * 16 + (lane & 15);
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
             float *yout = cur.shared ? a.y_shared : a.y_sorted;
 #pragma unroll
             for (int n = 0; n < NB; ++n) {
-                if ((n % kWavesMx) != wave) continue;
+                if (KSPLIT > 1 && (n % kWavesMx) != wave) continue;
                 const int c = cur.n0 + n * 16 + (lane & 15);
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
@@ -344,10 +359,10 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
                     }
             }
         }
-        lds_barrier();  // every wave has read `red` before the next item overwrites it
+        if (KSPLIT > 1) lds_barrier();  // every wave has read `red` before the next item overwrites it
         if (!nxt.valid) break;
         cur = nxt;
-        item += gridDim.x;
+        item += stride;
     }
 }
 
@@ -355,14 +370,15 @@ namespace {
 constexpr int kMxMB1 = FLINT_MX_MB1, kMxMB2 = FLINT_MX_MB2;
 constexpr int kMxNB1 = FLINT_MX_NB1, kMxNB2 = FLINT_MX_NB2;
 constexpr int kMxCK1 = FLINT_MX_CK1, kMxCK2 = FLINT_MX_CK2;
+constexpr int kMxKS1 = FLINT_MX_KS1, kMxKS2 = FLINT_MX_KS2;
 }  // namespace
 
 bool mx4_eligible(int T, int H, int I, int Is)
 {
-    // every item's reduction splits into 4 waves x an even number of steps,
+    // every item's reduction splits into its waves x an even number of steps,
     // and every column tile is whole
-    return T <= kMx4MaxT && H % (kWavesMx * 2 * kMxCK1) == 0 && I % (kWavesMx * 2 * kMxCK2) == 0 &&
-           Is % (kWavesMx * 2 * kMxCK2) == 0 && I % (kMxNB1 / 2 * 16) == 0 && Is % (kMxNB1 / 2 * 16) == 0 &&
+    return T <= kMx4MaxT && H % (kMxKS1 * 2 * kMxCK1) == 0 && I % (kMxKS2 * 2 * kMxCK2) == 0 &&
+           Is % (kMxKS2 * 2 * kMxCK2) == 0 && I % (kMxNB1 / 2 * 16) == 0 && Is % (kMxNB1 / 2 * 16) == 0 &&
            H % (kMxNB2 * 16) == 0;
 }
 
@@ -379,11 +395,14 @@ hipError_t launch_experts_mx4(const ExpertArgs &a, hipStream_t stream, const Mar
     const int max1 = ns1 + cap1 * (a.I / bn1);
     const int max2 = ns2 + cap2 * (a.H / bn2);
     const int grid_cap = FLINT_MX_GRID_ALL ? (1 << 30) : FLINT_MX_WGS * max(a.cus, 1);
-    hipError_t err = launch_k(k_expert_stream_mx4<kMxMB1, kMxNB1, kMxCK1, true>, min(grid_cap, max1), 256,
+    // work-groups to cover every item once: an item per work-group (KSPLIT 4) or per wave (1)
+    const int g1 = kMxKS1 > 1 ? max1 : (max1 + kWavesMx - 1) / kWavesMx;
+    const int g2 = kMxKS2 > 1 ? max2 : (max2 + kWavesMx - 1) / kWavesMx;
+    hipError_t err = launch_k(k_expert_stream_mx4<kMxMB1, kMxNB1, kMxCK1, true, kMxKS1>, min(grid_cap, g1), 256,
                               (size_t)(2 * cap1 + a.E + 1 + a.T * a.K) * 4, stream, marks ? marks[0] : Marks{}, a,
                               ns1);
     if (err != hipSuccess) return err;
-    return launch_k(k_expert_stream_mx4<kMxMB2, kMxNB2, kMxCK2, false>, min(grid_cap, max2), 256,
+    return launch_k(k_expert_stream_mx4<kMxMB2, kMxNB2, kMxCK2, false, kMxKS2>, min(grid_cap, g2), 256,
                     (size_t)(2 * cap2 + a.E + 1) * 4, stream, marks ? marks[1] : Marks{}, a, ns2);
 }
 

@@ -164,8 +164,8 @@ def test_forward_mx4_refusals(lib):
     assert _forward_mx4(lib, flint_dims(dtype=api.F32), 32) == api.UNSUPPORTED  # bf16 activations only
     assert _forward_mx4(lib, d, 513) == api.UNSUPPORTED  # small batches only
     assert _forward_mx4(lib, flint_dims(hidden=1536), 32) == api.UNSUPPORTED  # H % 1024
-    assert _forward_mx4(lib, flint_dims(inter=256), 32) == api.UNSUPPORTED  # I % 512
-    assert _forward_mx4(lib, flint_dims(shared_inter=768), 32) == api.UNSUPPORTED  # Is % 512
+    assert _forward_mx4(lib, flint_dims(inter=128), 32) == api.UNSUPPORTED  # I % 256
+    assert _forward_mx4(lib, flint_dims(shared_inter=640), 32) == api.UNSUPPORTED  # Is % 256
     assert _forward_mx4(lib, d, 32, x=None) == api.INVALID_ARG
     assert _forward_mx4(lib, d, 32, ws_bytes=api.flint_moe_workspace_bytes(d, 32) - 1) == \
         api.WORKSPACE_TOO_SMALL
