@@ -122,44 +122,6 @@ struct MxItem {
     int row0, row_end, n0, shared, valid;
 };
 
-// Work-group barrier that waits for this wave's LDS accesses only: global
-// loads in flight (the next item's first step) stay in flight across it.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// The four waves' partial sums added in wave order; every wave gets the total.
-template <int MB, int NB>
-__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[MB][NB], float *red)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    f32x4 *r4 = reinterpret_cast<f32x4 *>(red);
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int n = 0; n < NB; ++n) r4[((wave * MB + m) * NB + n) * 64 + lane] = acc[m][n];
-    lds_barrier();
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-            f32x4 t = r4[(m * NB + n) * 64 + lane];
-#pragma unroll
-            for (int w = 1; w < kWavesMx; ++w) {
-                const f32x4 v = r4[((w * MB + m) * NB + n) * 64 + lane];
-                t[0] += v[0];
-                t[1] += v[1];
-                t[2] += v[2];
-                t[3] += v[3];
-            }
-            acc[m][n] = t;
-        }
-}
-
 }  // namespace
 
 // GATE_UP: gate/up + SwiGLU -> h (bf16);  otherwise: down -> y (float32).
@@ -327,7 +289,7 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
             compute(rb);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (KSPLIT > 1) reduce_waves<MB, NB>(acc, red);
+        if (KSPLIT > 1) splitk_reduce<kWavesMx, MB, NB>(acc, red);
         if (GATE_UP) {
             uint16_t *hout = cur.shared ? (uint16_t *)a.h_shared : (uint16_t *)a.h_sorted;
             const int width = cur.shared ? a.Is : a.I;
@@ -359,7 +321,7 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
                     }
             }
         }
-        if (KSPLIT > 1) lds_barrier();  // every wave has read `red` before the next item overwrites it
+        if (KSPLIT > 1) __syncthreads();  // every wave has read `red` before the next item overwrites it
         if (!nxt.valid) break;
         cur = nxt;
         item += stride;
