@@ -333,6 +333,41 @@ int oracle_forward(const oracle_dims *d, int T, const float *x, const float *wr,
 }
 
 /* ------------------------------------------------------------------------ */
+/* A dense MLP layer for T tokens (the model's first two layers are dense MLPs,
+ * about 75M parameters together; serving-kit review, "The architecture, from
+ * the config").  Reading: the same gated three-matrix form as an expert, of
+ * width I (6144 fits the page's count: 2 * 3 * 2048 * 6144 = 75.5M), h stored
+ * in the layer's dtype, out[t] = float32(W_down (silu(W_gate x_t) * (W_up x_t))).
+ * Layouts: gate/up [I][H], down [H][I]. */
+int oracle_dense_mlp(int T, int H, int I, int h_is_bf16, const float *x, const float *wg, const float *wu,
+                     const float *wd, float *out)
+{
+    if (T < 0 || H <= 0 || I <= 0) return ORACLE_BAD_ARG;
+    if (T == 0) return ORACLE_OK;
+    if (!x || !wg || !wu || !wd || !out) return ORACLE_BAD_ARG;
+    oracle_dims d;
+    memset(&d, 0, sizeof d);
+    d.hidden = H;  /* the fields expert_one reads */
+    d.h_is_bf16 = h_is_bf16;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < T; ++t) {
+        double *hbuf = (double *)malloc(sizeof(double) * (size_t)I);
+        double *y = (double *)malloc(sizeof(double) * (size_t)H);
+        if (!hbuf || !y) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            expert_one(&d, I, x + (size_t)t * H, wg, wu, wd, hbuf, y);
+            for (int n = 0; n < H; ++n) out[(size_t)t * H + n] = (float)y[n];
+        }
+        free(hbuf);
+        free(y);
+    }
+    return bad ? ORACLE_BAD_ARG : ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* RMSNorm between stacked layers (a workload choice, not from the pages):
  * x_next = bf16( y / sqrt(mean(y^2) + eps) ), unit gain, mean over H. */
 int oracle_rmsnorm(int T, int H, const float *in, double eps, float *out)

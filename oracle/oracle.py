@@ -91,8 +91,9 @@ class Oracle:
         lib.oracle_param_counts.argtypes = [D, P]
         lib.oracle_mx4_dequant.argtypes = [ctypes.c_int64, ctypes.c_int, P, P, P]
         lib.oracle_mx4_untile.argtypes = [ctypes.c_int64, ctypes.c_int, P, P, P, P]
+        lib.oracle_dense_mlp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         for f in ("oracle_route", "oracle_scores", "oracle_dispatch", "oracle_forward",
-                  "oracle_rmsnorm", "oracle_mx4_dequant", "oracle_mx4_untile"):
+                  "oracle_rmsnorm", "oracle_mx4_dequant", "oracle_mx4_untile", "oracle_dense_mlp"):
             getattr(lib, f).restype = ctypes.c_int
         lib.oracle_round_bf16.restype = None
         lib.oracle_param_counts.restype = None
@@ -185,6 +186,20 @@ class Oracle:
         _check(self.lib.oracle_mx4_dequant(rows, n, _p(codes), _p(scales), _p(out)), "oracle_mx4_dequant")
         return out
 
+    def dense_mlp(self, x, w_gate, w_up, w_down, h_bf16=True):
+        """A dense gated MLP layer (see flint_oracle.c): x [T, H], gate/up [I, H],
+        down [H, I] -> float32 [T, H]; h rounded to bf16 (h_bf16) or float32."""
+        x = _f32(x)
+        wg, wu, wd = _f32(w_gate), _f32(w_up), _f32(w_down)
+        T, H = x.shape
+        I = wg.shape[0]
+        if wg.shape != (I, H) or wu.shape != (I, H) or wd.shape != (H, I):
+            raise ValueError("dense_mlp: gate/up [I, H] and down [H, I]")
+        out = np.zeros((T, H), np.float32)
+        _check(self.lib.oracle_dense_mlp(T, H, I, 1 if h_bf16 else 0, _p(x), _p(wg), _p(wu), _p(wd), _p(out)),
+               "oracle_dense_mlp")
+        return out
+
     def mx4_untile(self, codes, scales):
         """The tiled byte order of the library's MXFP4 arrays back to row-major.
         A tile is 16 rows x one 32-element block: codes [..., R/16, n/32, 16, 16]
@@ -273,6 +288,10 @@ def mx4_dequant(codes, scales):
 
 def mx4_untile(codes, scales):
     return default().mx4_untile(codes, scales)
+
+
+def dense_mlp(x, w_gate, w_up, w_down, h_bf16=True):
+    return default().dense_mlp(x, w_gate, w_up, w_down, h_bf16)
 
 
 def mx4_dequant_tiled(codes, scales):

@@ -432,8 +432,66 @@ def pin_mx4_tiled_layout(orc):
     assert c2.shape == (2, 32, 32) and c2[1, 0, 0] == 9 and np.count_nonzero(c2) == 1
 
 
+DENSE_INTER = 6144  # dense MLP width: not printed; the page's ~75M for two layers fits it
+
+
+def pin_dense_param_count(orc):
+    # two dense layers of the gated three-matrix form at hidden 2048, width 6144:
+    # the page's "about 75M" (a two-matrix form would give ~50M)
+    g = json.load(open(os.path.join(GOLDEN, "flint_param_counts.json")))
+    H, L = g["shape"]["hidden"], g["shape"]["dense_layers"]
+    printed = g["printed"]["two_dense_layers_millions"]
+    assert round(L * 3 * H * DENSE_INTER / 1e6) == printed
+    assert round(L * 2 * H * DENSE_INTER / 1e6) != printed
+    # a gated dense layer of this width runs: one token, weights of the right sizes
+    rng = np.random.default_rng(0)
+    H2, I2 = 64, 96
+    x = rng.standard_normal((1, H2)).astype(np.float32)
+    out = orc.dense_mlp(x, rng.standard_normal((I2, H2)).astype(np.float32) * 0.1,
+                        rng.standard_normal((I2, H2)).astype(np.float32) * 0.1,
+                        rng.standard_normal((H2, I2)).astype(np.float32) * 0.1)
+    assert out.shape == (1, H2) and np.all(np.isfinite(out))
+
+
+def pin_dense_closed_form(orc):
+    # H = 2, I = 1, x = (1, 0): g = ln 3, u = 2, silu(g) = (3/4) ln 3, h = (3/2) ln 3,
+    # down (1, -1/2) -> out = ((3/2) ln 3, -(3/4) ln 3); bf16 h is 211/128.
+    x = np.array([[1.0, 0.0]], np.float32)
+    wg = np.array([[_LN3, 0.0]], np.float32)
+    wu = np.array([[2.0, 0.0]], np.float32)
+    wd = np.array([[1.0], [-0.5]], np.float32)
+    out = orc.dense_mlp(x, wg, wu, wd, h_bf16=False)
+    np.testing.assert_allclose(out[0], [1.5 * _LN3, -0.75 * _LN3], rtol=1e-6)
+    out = orc.dense_mlp(x, wg, wu, wd, h_bf16=True)
+    np.testing.assert_array_equal(out[0], np.float32([211 / 128, -211 / 256]))
+    # tokens are independent: a batch gives each row's single-token result
+    rng = np.random.default_rng(5)
+    xs = rng.standard_normal((3, 2)).astype(np.float32)
+    batch = orc.dense_mlp(xs, wg, wu, wd)
+    for t in range(3):
+        np.testing.assert_array_equal(batch[t], orc.dense_mlp(xs[t:t + 1], wg, wu, wd)[0])
+
+
+def pin_dense_is_the_shared_expert_alone(orc):
+    # a MoE layer whose routed experts are all zero is its shared expert alone,
+    # i.e. a dense MLP with the shared expert's weights
+    rng = np.random.default_rng(9)
+    T, H, E, K, I, Is = 5, 32, 4, 2, 16, 48
+    w = {"router": rng.standard_normal((E, H)).astype(np.float32), "bias": None,
+         "gate": np.zeros((E, I, H), np.float32), "up": np.zeros((E, I, H), np.float32),
+         "down": np.zeros((E, H, I), np.float32),
+         "shared_gate": rng.standard_normal((Is, H)).astype(np.float32) * 0.2,
+         "shared_up": rng.standard_normal((Is, H)).astype(np.float32) * 0.2,
+         "shared_down": rng.standard_normal((H, Is)).astype(np.float32) * 0.2}
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    layer, _, _, _ = orc.forward(dims(H, E, K, I, Is, True), x, w)
+    dense = orc.dense_mlp(x, w["shared_gate"], w["shared_up"], w["shared_down"], h_bf16=True)
+    np.testing.assert_array_equal(layer, dense)
+
+
 ALL_PINS = [pin_param_counts, pin_bf16_rounding, pin_routing_hand_top2, pin_routing_hand_all,
             pin_routing_equal_logits, pin_routing_tie_break, pin_routing_limits, pin_routing_bias,
             pin_routing_library, pin_expert_closed_form, pin_bf16_intermediate, pin_dense_mixture,
             pin_shared_split, pin_token_permutation, pin_dispatch_hand, pin_dispatch_invariants,
-            pin_rmsnorm, pin_mx4_element_table, pin_mx4_scale, pin_mx4_layout, pin_mx4_tiled_layout]
+            pin_rmsnorm, pin_mx4_element_table, pin_mx4_scale, pin_mx4_layout, pin_mx4_tiled_layout,
+            pin_dense_param_count, pin_dense_closed_form, pin_dense_is_the_shared_expert_alone]

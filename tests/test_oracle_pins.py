@@ -68,6 +68,9 @@ MUTANTS = [
      "const int64_t tile = kb * (rows / 16) + rb;"),
     ("mx4_untile_row_byte_swapped", "codes_t[(tile * 16 + r) * 16 + j]", "codes_t[(tile * 16 + j) * 16 + r]"),
     ("mx4_untile_scale_rows_reversed", "= scales_t[tile * 16 + r];", "= scales_t[tile * 16 + 15 - r];"),
+    ("dense_h_always_f32", "d.h_is_bf16 = h_is_bf16;", "d.h_is_bf16 = 0;"),
+    ("dense_token_stride", "expert_one(&d, I, x + (size_t)t * H, wg, wu, wd, hbuf, y);",
+     "expert_one(&d, I, x, wg, wu, wd, hbuf, y);"),
 ]
 
 
