@@ -1,6 +1,7 @@
 """Benchmark of the Flint MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode32|prefill4096|skew16384|stack47|toy]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode32|prefill4096|skew16384|stack47|toy|decode32_mx4|dense32|dense4096]
 
 A step is one pass of the whole layer (router, top-k, dispatch, gate/up +
 SwiGLU, down, combine; for stack47 all 47 layers with RMSNorm between them) over
@@ -184,6 +185,114 @@ def cpu_baseline(wl, w_dev, x_dev, target_s):
                       f"in fp64, repeated {reps}x over {el:.1f} s"}
 
 
+def bench_dense(args, wl):
+    """The dense MLP layer (flint_dense_mlp): same timing scheme as the MoE layer,
+    stages gate/up, down and output; every step reads all of the layer's weights."""
+    import torch
+
+    from routed_expert_ffn_flint_amd import _lib, api, inputs
+
+    lib = _lib.load()
+    dd = api.dense_dims_of(wl)
+    T, H, I = wl.T, wl.hidden, wl.inter
+    eb = 2 if wl.bf16 else 4
+    n_copies = max(1, args.copies)
+    layers = [inputs.make_dense(wl, c, "cuda") for c in range(n_copies)]
+    x = inputs.make_tokens(wl, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = api.dense_workspace(dd, T)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptrs = [[ctypes.c_void_p(w[k].data_ptr()) for k in ("gate", "up", "down")] for w in layers]
+
+    def step(i, events=None):
+        arr = None if events is None else (ctypes.c_void_p * 6)(*[e.value for e in events])
+        g, u, dn = ptrs[i % n_copies]
+        st = lib.flint_dense_mlp(ctypes.byref(dd), T, ctypes.c_void_p(x.data_ptr()), g, u, dn,
+                                 ctypes.c_void_p(out.data_ptr()), api.F32, ctypes.c_void_p(ws.data_ptr()),
+                                 ws.numel(), sp, arr)
+        if st != 0:
+            raise api.FlintError(st, "flint_dense_mlp")
+
+    for i in range(args.warmup):
+        step(i)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+
+    hev = HipEvents()
+    n_prof = min(args.steps, 100)
+    ev_sets = [hev.create(6) for _ in range(n_prof)]
+    for i in range(n_prof):
+        step(i, ev_sets[i])
+    torch.cuda.synchronize()
+    names = ["gate_up", "down", "output"]
+    stage_us = {n: float(np.mean([hev.ms(evs[2 * j], evs[2 * j + 1]) for evs in ev_sets]) * 1e3)
+                for j, n in enumerate(names)}
+    for evs in ev_sets:
+        hev.destroy(evs)
+
+    gu_bytes = 2 * I * H * eb + T * H * eb + T * I * eb
+    gu_flops = 4 * T * I * H
+    layer_bytes = 3 * I * H * eb + T * H * eb + T * H * 4
+    layer_flops = 6 * T * I * H
+    big = T >= 2048
+    kernel = "k_expert_stream" if T <= STREAM_MAX_T else "k_tiled"
+    digest = sources_digest(kernel)
+    kname = f"{kernel}<gate/up> (gate/up GEMM + SwiGLU of the dense layer)"
+    traffic = counters_traffic(kernel, wl.name, digest)
+    if big:
+        achieved = gu_flops / (stage_us["gate_up"] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic, "kernel": kname,
+                    "per_launch": {"flops": gu_flops, "bytes": gu_bytes, "mean_us": stage_us["gate_up"]}}
+    else:
+        achieved = gu_bytes / (stage_us["gate_up"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kname,
+                    "per_launch": {"bytes": gu_bytes, "mean_us": stage_us["gate_up"]}}
+    roofline["sources_sha256"] = digest
+    lt = ms / 1e3
+    result = {
+        "metric": "dense MLP layer tokens/s (bf16, H=2048, width 6144) + % HBM/MFMA roofline",
+        "value": T / lt, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.bf16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: one dense gated MLP layer, T={T}, H={H}, width {I}", "T": T,
+                   "weight_copies": n_copies, "graph": False, "wall_s": wall},
+        "roofline": roofline,
+        "layer_roofline": {"hbm_GBs": layer_bytes / lt / 1e9, "hbm_frac": layer_bytes / lt / 1e9 / HBM_PEAK_GBS,
+                           "mfma_TFLOPs": layer_flops / lt / 1e12,
+                           "mfma_frac": layer_flops / lt / 1e12 / BF16_PEAK_TFLOPS,
+                           "algorithmic_bytes": layer_bytes, "flops": layer_flops},
+        "stages_us": stage_us,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        o = orc.default()
+        w0 = {k: inputs.to_numpy_f32(v) for k, v in layers[0].items()}
+        n_tok = min(T, 32)
+        xh = inputs.to_numpy_f32(x[:n_tok])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            o.dense_mlp(xh, w0["gate"], w0["up"], w0["down"], h_bf16=wl.bf16)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        result["cpu_baseline"] = {"value": reps * n_tok / el, "unit": "tokens/s", "cores": o.threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{wl.name} layer (weight copy 0), the first {n_tok} tokens, fp64, "
+                                            f"repeated {reps}x over {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -199,6 +308,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     lib = _lib.load()
     wl = inputs.WORKLOADS[args.workload]
+    if wl.dense:
+        bench_dense(args, wl)
+        return
     d = api.dims_of(wl)
     dev = "cuda"
     torch.cuda.set_device(0)

@@ -204,6 +204,36 @@ flint_status flint_moe_forward_mx4(const flint_moe_dims *dims, int32_t T, const 
                                    float *topk_w_out, void *ws, size_t ws_bytes, void *stream,
                                    void *const *events);
 
+/* ---- Dense MLP layer -------------------------------------------------------
+ * The model's first two layers are dense MLPs (serving-kit review, "The
+ * architecture, from the config": two dense layers, about 75M parameters
+ * together; no width is given).  Same gated three-matrix form as an expert,
+ * width `inter` (6144 fits the page's count at hidden 2048):
+ *   out[t] = W_down (silu(W_gate x_t) * (W_up x_t)),
+ * h rounded to dtype, float32 accumulation (the shared expert's kernels).
+ *   dims.hidden H: multiple of 64, at most 8192; dims.inter I: multiple of 64,
+ *   at most 16384; dims.dtype F32 or BF16.
+ *   x [T][H] dtype; gate, up [I][H] dtype; down [H][I] dtype; out [T][H]
+ *   out_dtype (F32, or BF16 rounded to nearest even) -- device pointers,
+ *   16-byte aligned, caller-owned; weights and x are read only.
+ *   ws: caller-owned device scratch of flint_dense_workspace_bytes(dims, T)
+ *   bytes, 256-byte aligned.
+ *   events: NULL or 6 hipEvent_t handles: start/stop of the gate/up, down and
+ *   output stages (the output stage is empty, its events stamped at the down
+ *   stage's end, when out_dtype is F32: the down stage writes out directly).
+ * Errors as for flint_moe_forward; T = 0 is a no-op. */
+typedef struct {
+    int32_t hidden;    /* H */
+    int32_t inter;     /* I */
+    flint_dtype dtype; /* x, weights and h */
+} flint_dense_dims;
+
+size_t flint_dense_workspace_bytes(const flint_dense_dims *dims, int32_t T);
+
+flint_status flint_dense_mlp(const flint_dense_dims *dims, int32_t T, const void *x, const void *gate,
+                             const void *up, const void *down, void *out, flint_dtype out_dtype, void *ws,
+                             size_t ws_bytes, void *stream, void *const *events);
+
 /* RMSNorm between stacked MoE layers (unit gain): out = bf16(in / sqrt(mean(in^2) + eps)),
  * the mean over each row of H values.  in [T][H] float32, out [T][H] bf16.
  * H must be a multiple of 64 and at most 8192.  This joins consecutive layers in

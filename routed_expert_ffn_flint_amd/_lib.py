@@ -35,8 +35,13 @@ class WeightsMx4(ctypes.Structure):
         for name in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down") for part in ("q", "s")]
 
 
+class DenseDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
 EXPORTS = ("flint_status_string", "flint_moe_workspace_bytes", "flint_moe_route", "flint_moe_dispatch",
-           "flint_moe_forward", "flint_moe_forward_profiled", "flint_moe_forward_mx4", "flint_rmsnorm")
+           "flint_moe_forward", "flint_moe_forward_profiled", "flint_moe_forward_mx4",
+           "flint_dense_workspace_bytes", "flint_dense_mlp", "flint_rmsnorm")
 
 
 def load():
@@ -65,6 +70,11 @@ def load():
     lib.flint_moe_forward_profiled.restype = I32
     lib.flint_moe_forward_mx4.argtypes = [D, I32, P, ctypes.POINTER(WeightsMx4), P, I32, P, P, P, SZ, P, P]
     lib.flint_moe_forward_mx4.restype = I32
+    DD = ctypes.POINTER(DenseDims)
+    lib.flint_dense_workspace_bytes.argtypes = [DD, I32]
+    lib.flint_dense_workspace_bytes.restype = SZ
+    lib.flint_dense_mlp.argtypes = [DD, I32, P, P, P, P, P, I32, P, SZ, P, P]
+    lib.flint_dense_mlp.restype = I32
     lib.flint_rmsnorm.argtypes = [I32, I32, P, P, ctypes.c_float, P]
     lib.flint_rmsnorm.restype = I32
     _lib = lib

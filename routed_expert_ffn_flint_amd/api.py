@@ -12,7 +12,7 @@ import ctypes
 
 import torch
 
-from ._lib import Dims, Weights, WeightsMx4, load
+from ._lib import DenseDims, Dims, Weights, WeightsMx4, load
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, DEVICE_ERROR = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
@@ -37,6 +37,11 @@ def make_dims(hidden, n_experts, top_k, inter, shared_inter, dtype) -> Dims:
 def dims_of(wl) -> Dims:
     """Dims of an inputs.Workload."""
     return make_dims(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, BF16 if wl.bf16 else F32)
+
+
+def dense_dims_of(wl) -> DenseDims:
+    """DenseDims of a dense workload (inputs.Workload with dense=True)."""
+    return DenseDims(hidden=wl.hidden, inter=wl.inter, dtype=BF16 if wl.bf16 else F32)
 
 
 def _ptr(t):
@@ -198,6 +203,54 @@ def flint_moe_forward_mx4(d: Dims, x, weights, out, topk_idx_out=None, topk_w_ou
                                       0 if ws is None else ws.numel(), _stream(stream), arr)
     if st != OK:
         raise FlintError(st, "flint_moe_forward_mx4")
+
+
+def flint_dense_workspace_bytes(dd: DenseDims, T: int) -> int:
+    return int(load().flint_dense_workspace_bytes(ctypes.byref(dd), int(T)))
+
+
+def dense_workspace(dd: DenseDims, T: int, device="cuda") -> torch.Tensor:
+    n = flint_dense_workspace_bytes(dd, T)
+    if n == 0 and T > 0:
+        raise FlintError(UNSUPPORTED, "flint_dense_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def flint_dense_mlp(dd: DenseDims, x, gate, up, down, out, ws, stream=None, events=None):
+    """The dense gated MLP layer: x [T, H], gate/up [I, H], down [H, I] in
+    dd.dtype; out [T, H] float32 or bfloat16; events: None or 6 hipEvent_t
+    handles (start/stop of gate/up, down, output)."""
+    T = x.shape[0]
+    el = torch.bfloat16 if dd.dtype == BF16 else torch.float32
+    _check_tensor("x", x, el, (T, dd.hidden))
+    _check_tensor("gate", gate, el, (dd.inter, dd.hidden))
+    _check_tensor("up", up, el, (dd.inter, dd.hidden))
+    _check_tensor("down", down, el, (dd.hidden, dd.inter))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check_tensor("out", out, None, (T, dd.hidden))
+    _check_tensor("ws", ws, torch.uint8)
+    arr = None
+    if events is not None:
+        if len(events) != 6:
+            raise ValueError("events: 6 hipEvent_t handles (start/stop of 3 stages)")
+        arr = (ctypes.c_void_p * 6)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
+    st = load().flint_dense_mlp(ctypes.byref(dd), T, _ptr(x), _ptr(gate), _ptr(up), _ptr(down), _ptr(out),
+                                BF16 if out.dtype == torch.bfloat16 else F32, _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream), arr)
+    if st != OK:
+        raise FlintError(st, "flint_dense_mlp")
+
+
+def dense_mlp(x, gate, up, down, out_dtype=torch.float32, ws=None, stream=None):
+    """Allocates the output (and workspace) and runs flint_dense_mlp."""
+    T, H = x.shape
+    dd = DenseDims(hidden=H, inter=gate.shape[0], dtype=BF16 if x.dtype == torch.bfloat16 else F32)
+    out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    if ws is None:
+        ws = dense_workspace(dd, T, x.device)
+    flint_dense_mlp(dd, x, gate, up, down, out, ws, stream)
+    return out
 
 
 def flint_rmsnorm(inp, out, eps=1e-6, stream=None):

@@ -395,6 +395,91 @@ flint_status flint_moe_forward_mx4(const flint_moe_dims *d, int32_t T, const voi
                         stream, events);
 }
 
+}  // extern "C"
+
+namespace {
+
+flint_status check_dense(const flint_dense_dims *d, int32_t T)
+{
+    if (!d) return FLINT_INVALID_ARG;
+    if (d->dtype != FLINT_F32 && d->dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
+    if (d->hidden <= 0 || d->inter <= 0 || T < 0) return FLINT_INVALID_ARG;
+    if (d->hidden % 64 || d->inter % 64 || d->hidden > 8192 || d->inter > 16384) return FLINT_UNSUPPORTED;
+    if ((int64_t)T * (d->hidden > d->inter ? d->hidden : d->inter) >= (int64_t)1 << 40) return FLINT_UNSUPPORTED;
+    return FLINT_OK;
+}
+
+// A dense layer runs on the expert kernels as a layer with no routed experts
+// (K = 0, I = 0) whose shared expert has the dense width.
+Workspace dense_workspace(const flint_dense_dims *d, int32_t T, void *base)
+{
+    return plan_workspace(base, T, d->hidden, 1, 0, 0, d->inter, d->dtype == FLINT_BF16 ? 2 : 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t flint_dense_workspace_bytes(const flint_dense_dims *d, int32_t T)
+{
+    if (check_dense(d, T) != FLINT_OK) return 0;
+    return dense_workspace(d, T, nullptr).bytes;
+}
+
+flint_status flint_dense_mlp(const flint_dense_dims *d, int32_t T, const void *x, const void *gate,
+                             const void *up, const void *down, void *out, flint_dtype out_dtype, void *ws,
+                             size_t ws_bytes, void *stream, void *const *events)
+{
+    flint_status st = check_dense(d, T);
+    if (st != FLINT_OK) return st;
+    if (out_dtype != FLINT_F32 && out_dtype != FLINT_BF16) return FLINT_UNSUPPORTED;
+    if (T == 0) return FLINT_OK;
+    if (!x || !gate || !up || !down || !out) return FLINT_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(gate) || !aligned16(up) || !aligned16(down) || !aligned16(out))
+        return FLINT_UNSUPPORTED;
+    if (ws_bytes < flint_dense_workspace_bytes(d, T)) return FLINT_WORKSPACE_TOO_SMALL;
+    if (!ws) return FLINT_INVALID_ARG;
+    if (((uintptr_t)ws & (kAlign - 1)) != 0) return FLINT_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = d->dtype == FLINT_BF16;
+    Workspace w = dense_workspace(d, T, ws);
+    ExpertArgs e{};
+    e.bf16 = bf16;
+    e.T = T;
+    e.H = d->hidden;
+    e.E = 1;
+    e.K = 0;
+    e.I = 0;
+    e.Is = d->inter;
+    e.x = x;
+    e.shared_gate = gate;
+    e.shared_up = up;
+    e.shared_down = down;
+    e.offsets = w.offsets;
+    e.list1 = w.list1;
+    e.list2 = w.list2;
+    e.meta = w.meta;
+    e.h_sorted = w.h_sorted;
+    e.h_shared = w.h_shared;
+    e.y_sorted = w.y_sorted;
+    e.out = out;
+    e.out_bf16 = out_dtype == FLINT_BF16;
+    // float32 output: the down stage writes it directly
+    e.skip_combine = out_dtype == FLINT_F32;
+    e.y_shared = e.skip_combine ? (float *)out : w.y_shared;
+    e.tiles = expert_tiles_for(T, d->hidden, 1, 0, 0, d->inter, bf16);
+    e.cus = device_cus();
+    Marks marks[3];
+    if (events)
+        for (int i = 0; i < 3; ++i) marks[i] = Marks{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]};
+    if (launch_experts(e, s, events ? marks : nullptr) != hipSuccess) return FLINT_DEVICE_ERROR;
+    if (events && e.skip_combine) {
+        if (hipEventRecord(marks[2].start, s) != hipSuccess || hipEventRecord(marks[2].stop, s) != hipSuccess)
+            return FLINT_DEVICE_ERROR;
+    }
+    return FLINT_OK;
+}
+
 flint_status flint_rmsnorm(int32_t T, int32_t H, const float *in, void *out_bf16, float eps, void *stream)
 {
     if (T < 0 || H <= 0) return FLINT_INVALID_ARG;

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(WaveGrid<SPLIT>::THREADS) void k_gate_up(ExpertArgs
         item -= n_shared_items;
         const int ntn = a.I / BN;
         const int entry = item / ntn;
-        const int nlist = a.meta[0];
+        const int nlist = a.K == 0 ? 0 : a.meta[0];
         e = a.list1[2 * entry];  // inside the list's capacity; used only if entry < nlist
         row0 = a.list1[2 * entry + 1];
         if (entry >= nlist) return;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(WaveGrid<SPLIT>::THREADS) void k_down(ExpertArgs a,
     } else {
         item -= n_shared_items;
         const int entry = item / ntn;
-        const int nlist = a.meta[1];
+        const int nlist = a.K == 0 ? 0 : a.meta[1];
         e = a.list2[2 * entry];
         row0 = a.list2[2 * entry + 1];
         if (entry >= nlist) return;
@@ -253,15 +253,18 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
     // latency instead of one each.
     int slots[kMaxTopK];
     float w[kMaxTopK];
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-        const size_t i = (size_t)t * K + (k < K ? k : K - 1);
-        slots[k] = a.slot_of[i];
-        w[k] = a.topk_w[i];
-    }
     f32x4 y[kMaxTopK];
+    if (K > 0) {  // K = 0: a dense layer, the shared term alone
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) y[k] = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
+        for (int k = 0; k < kMaxTopK; ++k) {
+            const size_t i = (size_t)t * K + (k < K ? k : K - 1);
+            slots[k] = a.slot_of[i];
+            w[k] = a.topk_w[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+            y[k] = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
+    }
     const f32x4 ys = a.Is > 0 ? *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -317,13 +320,13 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
     if (a.mx4) {
         const hipError_t err = launch_experts_mx4(a, stream, marks);
         if (err != hipSuccess) return err;
-        return launch_k(k_combine, gc, 256, 0, stream, m3, a);
+        return a.skip_combine ? hipSuccess : launch_k(k_combine, gc, 256, 0, stream, m3, a);
     }
     if (t.stream || t.tiled) {
         const hipError_t err =
             t.stream ? launch_experts_stream(a, stream, marks) : launch_experts_tiled(a, stream, marks);
         if (err != hipSuccess) return err;
-        return launch_k(k_combine, gc, 256, 0, stream, m3, a);
+        return a.skip_combine ? hipSuccess : launch_k(k_combine, gc, 256, 0, stream, m3, a);
     }
     const int cap1 = list_capacity(a.T, a.K, a.E, t.bm1);
     const int cap2 = list_capacity(a.T, a.K, a.E, t.bm2);
@@ -345,7 +348,7 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
     else
         err = launch_k(k_down<DT, 4, 4, 1, 4, false>, g2, 256, 0, stream, m2, a, ns2);
     if (err != hipSuccess) return err;
-    return launch_k(k_combine, gc, 256, 0, stream, m3, a);
+    return a.skip_combine ? hipSuccess : launch_k(k_combine, gc, 256, 0, stream, m3, a);
 }
 
 hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks)

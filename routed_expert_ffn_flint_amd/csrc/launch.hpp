@@ -134,6 +134,7 @@ struct ExpertArgs {
     float *y_sorted, *y_shared;
     void *out;
     bool out_bf16;
+    bool skip_combine;  // the shared down stage writes the output itself (a dense layer, float32 out)
     ExpertTiles tiles;
     int cus;  // compute units of the device (sizes the persistent kernels' grids)
 };

@@ -72,7 +72,8 @@ __device__ __forceinline__ Tables load_tables(const ExpertArgs &a, const int32_t
     t.list = lds;
     t.offsets = lds + 2 * nlist;
     for (int i = threadIdx.x; i < 2 * nlist; i += blockDim.x) t.list[i] = glist[i];
-    for (int i = threadIdx.x; i <= a.E; i += blockDim.x) t.offsets[i] = a.offsets[i];
+    if (a.K > 0)  // a dense layer (K = 0) has shared items only and no dispatch tables
+        for (int i = threadIdx.x; i <= a.E; i += blockDim.x) t.offsets[i] = a.offsets[i];
     __syncthreads();
     return t;
 }
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256, GATE_UP ? FLINT_ST_WGS1 : FLINT_ST_WGS2) void 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kg = (lane >> 4) * 8;
     const int H = a.H;
-    const int nlist = GATE_UP ? a.meta[0] : a.meta[1];
+    const int nlist = GATE_UP ? (a.K > 0 ? a.meta[0] : 0) : (a.K > 0 ? a.meta[1] : 0);
     const Tables tab = load_tables(a, GATE_UP ? a.list1 : a.list2, nlist, dyn_lds);
 
     const int ntn_shared = GATE_UP ? a.Is / BN : (H + BN - 1) / BN;

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
     } else {
         const int ntn_shared = MODE == GATE_UP ? a.Is / (BN / 2) : (H + BN - 1) / BN;
         const int ntn_routed = MODE == GATE_UP ? a.I / (BN / 2) : (H + BN - 1) / BN;
-        const int nlist = MODE == GATE_UP ? a.meta[0] : a.meta[1];
+        const int nlist = MODE == GATE_UP ? (a.K > 0 ? a.meta[0] : 0) : (a.K > 0 ? a.meta[1] : 0);
         const int item = xcd_item(ta.n_shared + nlist * ntn_routed);
         if (item < 0) return;
         shared = item < ta.n_shared;

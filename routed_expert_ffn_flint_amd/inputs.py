@@ -14,6 +14,9 @@ here, so every tensor is drawn):
   stack47      T=256,   47 distinct layers, RMSNorm between layers,   seed 1
   decode32_mx4 decode32 with every expert matrix stored as MXFP4 (block-scaled
                4-bit, see mx4_quantize, in the tiled order of mx4_tile); router bf16
+  dense32      a dense gated MLP layer (the model's first two layers), T=32,
+               H=2048, width 6144, bf16, seed 0
+  dense4096    the same at T=4096
 
 Weights ~ N(0, 0.02^2), hidden states ~ N(0, 1), drawn in float32 and rounded
 to bf16 (round-to-nearest-even, torch's conversion) for the bf16 workloads.
@@ -51,6 +54,7 @@ class Workload:
     zipf_bias: bool = False
     layers: int = 1
     mx4: bool = False  # expert matrices stored as MXFP4 (router stays bf16)
+    dense: bool = False  # a dense gated MLP layer of width `inter` (no router, no experts)
 
     @property
     def torch_dtype(self):
@@ -64,6 +68,8 @@ WORKLOADS = {
     "skew16384": Workload("skew16384", 16384, 2048, 256, 6, 512, 1024, True, 0, zipf_bias=True),
     "stack47": Workload("stack47", 256, 2048, 256, 6, 512, 1024, True, 1, layers=47),
     "decode32_mx4": Workload("decode32_mx4", 32, 2048, 256, 6, 512, 1024, True, 0, mx4=True),
+    "dense32": Workload("dense32", 32, 2048, 0, 0, 6144, 0, True, 0, dense=True),
+    "dense4096": Workload("dense4096", 4096, 2048, 0, 0, 6144, 0, True, 0, dense=True),
 }
 
 EXPERT_MATRICES = ("gate", "up", "down", "shared_gate", "shared_up", "shared_down")
@@ -73,7 +79,8 @@ ZIPF_S = 1.1
 ZIPF_SCALE = 0.5
 
 _TENSOR_IDS = {"router": 1, "bias": 2, "gate": 3, "up": 4, "down": 5,
-               "shared_gate": 6, "shared_up": 7, "shared_down": 8, "x": 9}
+               "shared_gate": 6, "shared_up": 7, "shared_down": 8, "x": 9,
+               "dense_gate": 10, "dense_up": 11, "dense_down": 12}
 
 
 def _gen(seed: int, layer: int, tensor: str, device) -> torch.Generator:
@@ -161,6 +168,14 @@ def mx4_tile(codes: torch.Tensor, scales: torch.Tensor):
     return c, s
 
 
+def make_dense(wl: Workload, layer: int = 0, device="cpu") -> dict:
+    """Weights of a dense MLP layer: gate, up [I,H], down [H,I], N(0, 0.02^2)."""
+    H, I, dt, s = wl.hidden, wl.inter, wl.torch_dtype, wl.seed
+    return {"gate": _normal((I, H), WEIGHT_STD, dt, s, layer, "dense_gate", device),
+            "up": _normal((I, H), WEIGHT_STD, dt, s, layer, "dense_up", device),
+            "down": _normal((H, I), WEIGHT_STD, dt, s, layer, "dense_down", device)}
+
+
 def make_layer(wl: Workload, layer: int = 0, device="cpu", with_shared: bool = True) -> dict:
     """Weights of one layer as torch tensors on ``device``.
 
@@ -198,8 +213,8 @@ def make_tokens(wl: Workload, T: int | None = None, device="cpu", stream: int = 
 
 
 def custom(name="custom", T=8, hidden=64, n_experts=8, top_k=2, inter=64, shared_inter=64,
-           bf16=True, seed=0, zipf=False, layers=1, mx4=False) -> Workload:
-    return Workload(name, T, hidden, n_experts, top_k, inter, shared_inter, bf16, seed, zipf, layers, mx4)
+           bf16=True, seed=0, zipf=False, layers=1, mx4=False, dense=False) -> Workload:
+    return Workload(name, T, hidden, n_experts, top_k, inter, shared_inter, bf16, seed, zipf, layers, mx4, dense)
 
 
 def expected_distinct_experts(T: int, E: int = 256, K: int = 6) -> float:

@@ -183,3 +183,30 @@ def test_forward_mx4_refusals(lib):
     fields = {f"{n}_{p}": FAKE for n in ("gate", "up", "down") for p in ("q", "s")}
     w = _lib.WeightsMx4(router=FAKE, router_bias=None, **fields)
     assert _forward_mx4(lib, ns, 0, w=w) == api.OK
+
+
+def _dense(lib, dd, T, ws_bytes=None, x=FAKE, out_dtype=api.F32, ws=FAKE_WS):
+    if ws_bytes is None:
+        ws_bytes = lib.flint_dense_workspace_bytes(ctypes.byref(dd), T) if T >= 0 else 0
+    return lib.flint_dense_mlp(ctypes.byref(dd), T, x, FAKE, FAKE, FAKE, FAKE, out_dtype, ws, ws_bytes, None, None)
+
+
+def test_dense_mlp_refusals(lib):
+    dd = _lib.DenseDims(hidden=2048, inter=6144, dtype=api.BF16)
+    n32 = lib.flint_dense_workspace_bytes(ctypes.byref(dd), 32)
+    # h [T][I] bf16 and y [T][H] float32 at least
+    assert n32 >= 32 * 6144 * 2 + 32 * 2048 * 4
+    assert lib.flint_dense_workspace_bytes(ctypes.byref(dd), 64) > n32
+    assert _dense(lib, dd, 0) == api.OK  # no-op
+    assert _dense(lib, dd, -1) == api.INVALID_ARG
+    assert _dense(lib, _lib.DenseDims(hidden=2048, inter=6144, dtype=7), 32) == api.UNSUPPORTED
+    assert _dense(lib, _lib.DenseDims(hidden=2000, inter=6144, dtype=api.BF16), 32) == api.UNSUPPORTED
+    assert _dense(lib, _lib.DenseDims(hidden=2048, inter=6100, dtype=api.BF16), 32) == api.UNSUPPORTED
+    assert _dense(lib, _lib.DenseDims(hidden=2048, inter=16448, dtype=api.BF16), 32) == api.UNSUPPORTED
+    assert _dense(lib, _lib.DenseDims(hidden=0, inter=6144, dtype=api.BF16), 32) == api.INVALID_ARG
+    assert _dense(lib, dd, 32, x=None) == api.INVALID_ARG
+    assert _dense(lib, dd, 32, x=FAKE + 4) == api.UNSUPPORTED  # 16-byte alignment
+    assert _dense(lib, dd, 32, out_dtype=5) == api.UNSUPPORTED
+    assert _dense(lib, dd, 32, ws_bytes=n32 - 1) == api.WORKSPACE_TOO_SMALL
+    assert _dense(lib, dd, 32, ws=FAKE_WS + 16) == api.UNSUPPORTED  # 256-byte aligned workspace
+    assert _dense(lib, dd, 32, ws=None) == api.INVALID_ARG

@@ -327,3 +327,64 @@ def test_mx4_decode32_every_token_and_deterministic():
     again, _, _ = G.gpu_layer(wl, w, x)
     assert torch.equal(st["out"].view(torch.int32), again.view(torch.int32))
     print(f"decode32_mx4: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
+
+
+# ---- dense MLP layer (flint_dense_mlp) ---------------------------------------
+
+DENSE_CASES = [
+    # name,         T,    H,    I,    bf16
+    ("d_t1",        1,    128,  192,  True),
+    ("d_t33",       33,   256,  320,  True),
+    ("d_t7_f32",    7,    128,  64,   False),
+    ("d_t600",      600,  256,  512,  True),    # large-batch (tiled) kernels
+    ("d_t700_f32",  700,  128,  128,  False),   # float32 large-batch kernels
+    ("d_flint32",   32,   2048, 6144, True),    # the dense layer's width, decode batch
+]
+
+
+def _dense(wl, device="cuda"):
+    if wl.inter * wl.hidden <= (1 << 22):
+        w = {k: v.to(device) for k, v in inputs.make_dense(wl, 0, "cpu").items()}
+        x = inputs.make_tokens(wl, device="cpu").to(device)
+    else:
+        w = inputs.make_dense(wl, 0, device)
+        x = inputs.make_tokens(wl, device=device)
+    return w, x
+
+
+def _dense_check(wl, w, x, rows=None, out_dtype=torch.float32):
+    out = api.dense_mlp(x, w["gate"], w["up"], w["down"], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.T) if rows is None else rows
+    ref = orc.dense_mlp(inputs.to_numpy_f32(x)[rows], inputs.to_numpy_f32(w["gate"]),
+                        inputs.to_numpy_f32(w["up"]), inputs.to_numpy_f32(w["down"]), h_bf16=wl.bf16)
+    got = out.float().cpu().numpy()[rows]
+    if out_dtype == torch.bfloat16:
+        ref = inputs.to_numpy_f32(torch.from_numpy(ref).to(torch.bfloat16))
+    rel = G.check_output(got, ref, wl.name)
+    return out, rel
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_every_token(case):
+    name, T, H, I, bf16 = case
+    wl = inputs.custom(name, T, H, 0, 0, I, 0, bf16, seed=13, dense=True)
+    w, x = _dense(wl)
+    out, rel = _dense_check(wl, w, x)
+    print(f"{name}: rel_err={rel:.3g}")
+    again = api.dense_mlp(x, w["gate"], w["up"], w["down"])
+    assert torch.equal(out.view(torch.int32), again.view(torch.int32))  # deterministic
+
+
+def test_dense_bf16_output():
+    wl = inputs.custom("d_bf16out", 45, 256, 0, 0, 384, 0, True, seed=2, dense=True)
+    w, x = _dense(wl)
+    _dense_check(wl, w, x, out_dtype=torch.bfloat16)
+
+
+def test_dense4096_sampled():
+    wl = inputs.WORKLOADS["dense4096"]
+    w, x = _dense(wl)
+    rows = np.unique(np.concatenate([np.arange(0, wl.T, 97), [wl.T - 1]]))
+    _, rel = _dense_check(wl, w, x, rows=rows)
+    print(f"dense4096: rel_err={rel:.3g} on {len(rows)} tokens")
