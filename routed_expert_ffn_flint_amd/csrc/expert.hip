@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf16)
 {
     if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
-        return ExpertTiles{stream_bm1(), 0, stream_bm2(), 0, true, true, false};
+        return ExpertTiles{stream_bm1(T), 0, stream_bm2(), 0, true, true, false};
     // Small batches (decode): split-k kernels over 32-row tiles, so that one
     // tile holds every row an expert gets and each weight is read once.
     if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};

@@ -144,7 +144,7 @@ hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *
 // Persistent streaming kernels (small batches, shapes whose H, I, Is split into
 // whole batches), a few work-groups per CU.
 bool stream_eligible(int T, int H, int I, int Is);
-int stream_bm1();
+int stream_bm1(int T);
 int stream_bm2();
 // marks (nullable): gate/up and down stages.
 hipError_t launch_experts_stream(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
