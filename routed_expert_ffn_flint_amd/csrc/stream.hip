@@ -10,15 +10,17 @@
 //   - a fixed grid of work-groups (a few per CU) walks the work items with a
 //     static stride, so per-group setup is paid once, not per tile;
 //   - each work-group first copies the dispatch tables (tile list, expert
-//     offsets, the expert-sorted token list) into LDS, so looking up an item's
-//     expert, rows and tokens costs LDS reads only;
+//     offsets) into LDS, so looking up an item's expert and rows costs LDS
+//     reads only (an item's tokens are read from the expert-sorted list in
+//     global memory when the item is set up, one item ahead);
 //   - each wave streams its quarter of the reduction dimension in batches of U
 //     32-wide slices, the next batch (of this item or of the next one) issued
 //     before the current batch's MFMAs, so weight loads stay in flight across
 //     item boundaries;
 //   - the four waves' partial sums are added in LDS in wave order (the result
 //     does not depend on timing).
-// Gate/up items: 32 rows x (NB/2)*16 channels of gate and of up, SwiGLU fused.
+// Gate/up items: MB*16 rows x (NB/2)*16 channels of gate and of up, SwiGLU
+// fused (16 x 16 + 16 for batches of up to 64 tokens, else 32 x 32 + 32).
 // Down items: 32 rows x NB*16 output columns.
 #include "gemm_core.hpp"
 #include "launch.hpp"
