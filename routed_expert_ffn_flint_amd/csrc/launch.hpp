@@ -166,7 +166,10 @@ bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16);
 hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
 // The router product on the same tiles (large bf16 batches).
 bool tiled_router_eligible(int T, int H, bool bf16);
-constexpr int kRouterSplits = 4;
+#ifndef FLINT_ROUTER_SPLITS
+#define FLINT_ROUTER_SPLITS 4
+#endif
+constexpr int kRouterSplits = FLINT_ROUTER_SPLITS;
 hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
                                float *logits, hipStream_t stream, Marks m);
 

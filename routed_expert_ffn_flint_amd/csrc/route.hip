@@ -20,6 +20,9 @@
 //   k_dispatch_scatter (more than one tile) slot = offset + tile base + rank.
 #include <climits>
 
+#ifndef FLINT_TOPK_WAVE_T
+#define FLINT_TOPK_WAVE_T 4096  // largest batch selected one token per wave (16 lanes per token above)
+#endif
 #ifndef FLINT_TOPK_WAVE
 #define FLINT_TOPK_WAVE 1  // T <= 1024: bitwise K-th-largest search (1) or sorted-list merges (0)
 #endif
@@ -526,7 +529,7 @@ hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks
     Marks first{m.start, a.dispatch ? nullptr : m.stop};
     hipError_t err = hipSuccess;
     if (a.compute_topk) {
-        err = a.T <= 1024 ? launch_k(FLINT_TOPK_WAVE ? k_topk_wave : k_topk<64>, (a.T + 3) / 4, 256, 0, stream, first, a)
+        err = a.T <= FLINT_TOPK_WAVE_T ? launch_k(FLINT_TOPK_WAVE ? k_topk_wave : k_topk<64>, (a.T + 3) / 4, 256, 0, stream, first, a)
                           : launch_k(k_topk<16>, (a.T + 15) / 16, 256, 0, stream, first, a);
         if (err != hipSuccess) return err;
         first.start = nullptr;

@@ -307,6 +307,7 @@ MX4_CASES = [
     ("mx4_t7_ns",  7,  1024, 8,  2, 512, 0,   False),
     ("mx4_t200",   200, 2048, 32, 6, 512, 1024, True),
     ("mx4_t9_i256", 9,  1024, 8,  2, 256, 256,  False),  # the smallest supported widths
+    ("mx4_t300",   300, 1024, 32, 6, 512, 512,  True),   # wide gate/up and down items
 ]
 
 
