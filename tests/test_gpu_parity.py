@@ -389,3 +389,33 @@ def test_dense4096_sampled():
     rows = np.unique(np.concatenate([np.arange(0, wl.T, 97), [wl.T - 1]]))
     _, rel = _dense_check(wl, w, x, rows=rows)
     print(f"dense4096: rel_err={rel:.3g} on {len(rows)} tokens")
+
+
+def test_mx4_scale_extremes_and_nan_blocks():
+    """MXFP4 scales away from the quantiser's range: every block's scale byte
+    redrawn in 127 +- 12, some blocks at 0 (2^-127, subnormal weights), and one
+    block of one routed expert at 255 (NaN): the GPU must agree with the oracle
+    wherever the oracle is finite, and be NaN exactly where it is NaN."""
+    wl = inputs.custom("mx4_scales", 40, 1024, 8, 2, 512, 512, True, seed=21, mx4=True)
+    w, x = _layer(wl)
+    g = torch.Generator().manual_seed(4)
+    for k in ("gate", "up", "down", "shared_gate", "shared_up", "shared_down"):
+        s = w[k + "_s"]
+        new = torch.randint(115, 140, tuple(s.shape), generator=g, dtype=torch.int32).to(torch.uint8)
+        new.view(-1)[::97] = 0
+        s.copy_(new.to(s.device))
+    d = api.dims_of(wl)
+    idx, _ = api.route(d, x, w["router"], w.get("bias"))
+    hot = int(idx[0, 0])  # an expert token 0 uses
+    w["up_s"][hot, 0, 0, 3] = 255  # up row 3 of that expert, first block
+    out, gi, tw = G.gpu_layer(wl, w, x)
+    dd = G.oracle_dims(wl)
+    wh = G.host_weights_mx4(w)
+    ref, _, _, _ = orc.forward(dd, inputs.to_numpy_f32(x), wh, force_idx=gi.cpu().numpy())
+    got = out.float().cpu().numpy()
+    nan_ref = np.isnan(ref)
+    assert nan_ref[0].all()  # token 0 routes through the NaN block
+    np.testing.assert_array_equal(np.isnan(got), nan_ref)
+    fin = ~nan_ref.any(axis=1)
+    assert fin.sum() >= 5
+    G.check_output(got[fin], ref[fin], "mx4_scales")
