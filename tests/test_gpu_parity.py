@@ -330,6 +330,14 @@ def test_mx4_decode32_every_token_and_deterministic():
     print(f"decode32_mx4: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
 
 
+def test_mx4_largest_batch_every_token():
+    """The largest batch the MXFP4 entry point takes (T = 512), Flint shape."""
+    wl = inputs.custom("mx4_t512", 512, 2048, 256, 6, 512, 1024, True, seed=7, mx4=True)
+    w, x = _layer(wl)
+    st = G.parity_mx4(wl, w, x)
+    print(f"mx4_t512: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
+
+
 # ---- dense MLP layer (flint_dense_mlp) ---------------------------------------
 
 DENSE_CASES = [
