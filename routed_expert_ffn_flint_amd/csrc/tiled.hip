@@ -81,6 +81,9 @@ struct Cfg {
 #ifndef FLINT_TL_S_ST
 #define FLINT_TL_S_ST 5
 #endif
+#ifndef FLINT_TL_N_ST
+#define FLINT_TL_N_ST 4
+#endif
 #ifndef FLINT_TL_B_ST
 #define FLINT_TL_B_ST 4
 #endif
@@ -88,6 +91,7 @@ using CfgSmall = Cfg<128, 128, 64, 64, FLINT_TL_S_BK, FLINT_TL_S_ST>;  // 4 wave
 using CfgWide = Cfg<256, 128, 128, 64, 32, 6>;                         // 4 waves
 using CfgBig = Cfg<256, 256, 128, 128, 32, FLINT_TL_B_ST>;             // 4 waves
 using CfgBig8 = Cfg<256, 256, 128, 64, 32, FLINT_TL_B_ST>;             // 8 waves
+using CfgWideN = Cfg<128, 256, 64, 64, 32, FLINT_TL_N_ST>;              // 8 waves
 
 // Item of this work-group, or -1 (see the file comment).  Work-groups are
 // dealt to the XCDs round-robin (blockIdx.x % 8 is the XCD); the grid is sized
@@ -395,7 +399,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
 #define FLINT_TL_BIG_ROWS 256  // mean rows per expert from which the big configurations are used
 #endif
 #ifndef FLINT_TL_GU_SMALL
-#define FLINT_TL_GU_SMALL 0  // gate/up below that: 0 CfgSmall, 1 CfgWide
+#define FLINT_TL_GU_SMALL 6  // gate/up below that: 0 CfgSmall, 1 CfgWide, 6 CfgWideN (T = 4096: 290 -> 280 us)
 #endif
 #ifndef FLINT_TL_GU_BIG
 #define FLINT_TL_GU_BIG 3  // gate/up from there: 2 CfgBig, 3 CfgBig8 (or 0, 1)
@@ -412,7 +416,8 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
 
 namespace {
 
-int cfg_bm(int which) { return which >= 1 ? 256 : 128; }
+// which: 0 CfgSmall, 1 CfgWide, 2 CfgBig, 3 CfgBig8, 6 CfgWideN
+int cfg_bm(int which) { return which >= 1 && which <= 3 ? 256 : 128; }
 int cfg_bn(int which) { return which >= 2 ? 256 : 128; }
 
 bool big_batch(int T, int K, int E) { return (long long)T * K >= (long long)FLINT_TL_BIG_ROWS * E; }
@@ -444,6 +449,10 @@ hipError_t launch_mode(int which, const TiledArgs &ta, hipStream_t stream, Marks
     case 1: return launch_cfg<MODE, CfgWide>(ta, stream, m);
     case 2: return launch_cfg<MODE, CfgBig>(ta, stream, m);
     case 3: return launch_cfg<MODE, CfgBig8>(ta, stream, m);
+    case 6:
+        // 128 x 256 tiles (128 gate + 128 up channels): whole tiles of the widths, else 128 x 128
+        if (MODE != GATE_UP || (ta.e.I % 128 == 0 && ta.e.Is % 128 == 0)) return launch_cfg<MODE, CfgWideN>(ta, stream, m);
+        return launch_cfg<MODE, CfgSmall>(ta, stream, m);
     default: return launch_cfg<MODE, CfgSmall>(ta, stream, m);
     }
 }
@@ -454,7 +463,8 @@ bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16)
 {
     // whole k slices (H, I, Is); a gate/up tile takes BN/2 gate channels and
     // the same up channels
-    const int half = cfg_bn(gu_cfg(T, K, E)) / 2;
+    const int which = gu_cfg(T, K, E);
+    const int half = cfg_bn(which == 6 ? 0 : which) / 2;  // CfgWideN falls back to CfgSmall
     return bf16 && H % 64 == 0 && I % 64 == 0 && Is % 64 == 0 && I % half == 0 && Is % half == 0;
 }
 
