@@ -72,7 +72,7 @@ int list_capacity(int T, int K, int E, int bm)
     return (int)(pairs / bm + nonempty + 1);
 }
 
-Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int eb)
+Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int eb, int shared_splits)
 {
     Workspace w{};
     const size_t TK = (size_t)T * K;
@@ -109,7 +109,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     w.h_sorted = take(TK * I * eb);
     w.h_shared = take((size_t)T * Is * eb);
     w.y_sorted = (float *)take(TK * H * 4);
-    w.y_shared = (float *)take((size_t)T * H * 4);
+    w.y_shared = (float *)take((size_t)shared_splits * T * H * 4);
     w.bytes = off;
     return w;
 }
@@ -300,6 +300,7 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
     e.h_shared = w.h_shared;
     e.y_sorted = w.y_sorted;
     e.y_shared = w.y_shared;
+    e.shared_splits = 1;
     e.out = out;
     e.out_bf16 = out_dtype == FLINT_BF16;
     e.tiles = tiles;
@@ -410,10 +411,22 @@ flint_status check_dense(const flint_dense_dims *d, int32_t T)
 }
 
 // A dense layer runs on the expert kernels as a layer with no routed experts
-// (K = 0, I = 0) whose shared expert has the dense width.
+// (K = 0, I = 0) whose shared expert has the dense width.  On the streaming
+// kernels its down product has only H/32 column tiles per 32 rows, so the
+// reduction is split into `dense_splits` partial arrays that the combine adds.
+int dense_splits(const flint_dense_dims *d, int32_t T)
+{
+    if (T > kStreamMaxT || !stream_eligible(T, d->hidden, 0, d->inter)) return 1;
+    int best = 1;
+    for (int s = 2; s <= 8; ++s)  // whole, even batches of 32-wide slices per wave in every split
+        if (d->inter % s == 0 && stream_eligible(T, d->hidden, 0, d->inter / s)) best = s;
+    return best;
+}
+
 Workspace dense_workspace(const flint_dense_dims *d, int32_t T, void *base)
 {
-    return plan_workspace(base, T, d->hidden, 1, 0, 0, d->inter, d->dtype == FLINT_BF16 ? 2 : 4);
+    return plan_workspace(base, T, d->hidden, 1, 0, 0, d->inter, d->dtype == FLINT_BF16 ? 2 : 4,
+                          dense_splits(d, T));
 }
 
 }  // namespace
@@ -464,8 +477,9 @@ flint_status flint_dense_mlp(const flint_dense_dims *d, int32_t T, const void *x
     e.y_sorted = w.y_sorted;
     e.out = out;
     e.out_bf16 = out_dtype == FLINT_BF16;
-    // float32 output: the down stage writes it directly
-    e.skip_combine = out_dtype == FLINT_F32;
+    e.shared_splits = dense_splits(d, T);
+    // float32 output from a single down product: the down stage writes it directly
+    e.skip_combine = out_dtype == FLINT_F32 && e.shared_splits == 1;
     e.y_shared = e.skip_combine ? (float *)out : w.y_shared;
     e.tiles = expert_tiles_for(T, d->hidden, 1, 0, 0, d->inter, bf16);
     e.cus = device_cus();

@@ -267,6 +267,7 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
     }
     const f32x4 ys = a.Is > 0 ? *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nsplit = a.shared_splits > 1 ? a.shared_splits : 1;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
@@ -282,6 +283,13 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
         acc[1] += ys[1];
         acc[2] += ys[2];
         acc[3] += ys[3];
+        for (int sp = 1; sp < nsplit; ++sp) {  // the shared down product's other partial sums, in order
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(a.y_shared + ((size_t)sp * a.T + t) * H + c);
+            acc[0] += v[0];
+            acc[1] += v[1];
+            acc[2] += v[2];
+            acc[3] += v[3];
+        }
     }
     if (a.out_bf16) {
         uint16_t *o = (uint16_t *)a.out + (size_t)t * H + c;
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf16)
 {
     if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
-        return ExpertTiles{stream_bm1(T), 0, stream_bm2(), 0, true, true, false};
+        return ExpertTiles{stream_bm1(T, K), 0, stream_bm2(), 0, true, true, false};
     // Small batches (decode): split-k kernels over 32-row tiles, so that one
     // tile holds every row an expert gets and each weight is read once.
     if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};

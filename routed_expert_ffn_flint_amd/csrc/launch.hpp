@@ -85,7 +85,10 @@ struct Workspace {
 };
 
 // Computes the layout for (T, dims); with base == nullptr only .bytes is valid.
-Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int elem_bytes);
+// shared_splits: partial arrays of the shared expert's down product (y_shared
+// is [shared_splits][T][H]; see ExpertArgs::shared_splits).
+Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int elem_bytes,
+                         int shared_splits = 1);
 
 int list_capacity(int T, int K, int E, int bm);
 
@@ -132,6 +135,11 @@ struct ExpertArgs {
     const int32_t *list1, *list2, *meta;
     void *h_sorted, *h_shared;
     float *y_sorted, *y_shared;
+    // The shared expert's down product split over its reduction into this many
+    // partial arrays y_shared[s] (the streaming kernels only; 1 elsewhere), which
+    // the combine adds in order: a dense layer at decode sizes has too few
+    // column tiles to fill the chip otherwise.
+    int shared_splits;
     void *out;
     bool out_bf16;
     bool skip_combine;  // the shared down stage writes the output itself (a dense layer, float32 out)
@@ -144,7 +152,7 @@ hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *
 // Persistent streaming kernels (small batches, shapes whose H, I, Is split into
 // whole batches), a few work-groups per CU.
 bool stream_eligible(int T, int H, int I, int Is);
-int stream_bm1(int T);
+int stream_bm1(int T, int K);
 int stream_bm2();
 // marks (nullable): gate/up and down stages.
 hipError_t launch_experts_stream(const ExpertArgs &a, hipStream_t stream, const Marks *marks);

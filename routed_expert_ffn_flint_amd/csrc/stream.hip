@@ -102,6 +102,7 @@ struct Item {
     int s0;          // first slice of this wave
     int nbatch;      // batches of U slices for this wave
     int row0, row_end, n0, kdim;
+    int ysplit;      // shared down items: which partial array of y_shared
     int shared;      // 1: shared-expert item
     int valid;
 };
@@ -135,13 +136,21 @@ __global__ __launch_bounds__(256, GATE_UP ? FLINT_ST_WGS1 : FLINT_ST_WGS2) void 
         it.valid = item < n_items;
         if (!it.valid) item = 0;  // a valid item's addresses, used only as dummy prefetch targets
         int e = 0, nt;
+        int klen, kfirst = 0;  // this item's reduction: slices [kfirst, kfirst + klen/32)
         const S *wa, *wb;  // gate/up (GATE_UP) or the down matrix (wa)
+        it.ysplit = 0;
         if (item < n_shared_items) {
+            // shared down items come in shared_splits parts of the reduction
+            const int nsplit = GATE_UP ? 1 : (a.shared_splits > 1 ? a.shared_splits : 1);
+            const int sh = item / nsplit;
+            it.ysplit = item % nsplit;
             it.shared = 1;
-            it.row0 = (item / ntn_shared) * BM;
-            nt = item % ntn_shared;
+            it.row0 = (sh / ntn_shared) * BM;
+            nt = sh % ntn_shared;
             it.row_end = a.T;
             it.kdim = GATE_UP ? H : a.Is;
+            klen = it.kdim / nsplit;
+            kfirst = it.ysplit * (klen / 32);
             wa = GATE_UP ? (const S *)a.shared_gate : (const S *)a.shared_down;
             wb = (const S *)a.shared_up;
         } else {
@@ -153,12 +162,13 @@ __global__ __launch_bounds__(256, GATE_UP ? FLINT_ST_WGS1 : FLINT_ST_WGS2) void 
             it.row0 = tab.list[2 * entry + 1];
             it.row_end = tab.offsets[e + 1];
             it.kdim = GATE_UP ? H : a.I;
+            klen = it.kdim;
             wa = GATE_UP ? (const S *)a.gate + (size_t)e * a.I * H : (const S *)a.down + (size_t)e * H * a.I;
             wb = GATE_UP ? (const S *)a.up + (size_t)e * a.I * H : nullptr;
         }
         it.n0 = nt * BN;
-        const int per = it.kdim / 32 / kWaves;  // slices per wave (the launcher checks divisibility)
-        it.s0 = wave * per;
+        const int per = klen / 32 / kWaves;  // slices per wave (the launcher checks divisibility)
+        it.s0 = kfirst + wave * per;
         it.nbatch = per / U;
         if (GATE_UP) {
 #pragma unroll
@@ -257,7 +267,7 @@ __global__ __launch_bounds__(256, GATE_UP ? FLINT_ST_WGS1 : FLINT_ST_WGS2) void 
                     }
             }
         } else {
-            float *yout = cur.shared ? a.y_shared : a.y_sorted;
+            float *yout = cur.shared ? a.y_shared + (size_t)cur.ysplit * a.T * H : a.y_sorted;
 #pragma unroll
             for (int n = 0; n < NB; ++n) {
                 if ((n % kWaves) != wave) continue;
@@ -302,14 +312,16 @@ bool stream_eligible(int T, int H, int I, int Is)
 {
     return T <= FLINT_ST_MAXT && unroll_gate_up(H) > 0 && unroll_down(I, Is) > 0;
 }
-static bool small_batch(int T) { return T <= FLINT_ST_SMALL_T; }
-int stream_bm1(int T) { return (small_batch(T) ? FLINT_ST_MB1S : FLINT_ST_MB1) * 16; }
+// (routed layers only: a dense layer's gate/up items are all shared-expert
+// items, and there the 32 x 64 items measured faster at T = 32, 18 vs 22 us)
+static bool small_batch(int T, int K) { return T <= FLINT_ST_SMALL_T && K > 0; }
+int stream_bm1(int T, int K) { return (small_batch(T, K) ? FLINT_ST_MB1S : FLINT_ST_MB1) * 16; }
 int stream_bm2() { return FLINT_ST_MB2 * 16; }
 
 template <typename DT, int U, bool GATE_UP>
 static hipError_t launch_one(const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream, Marks m)
 {
-    if (GATE_UP && small_batch(a.T))
+    if (GATE_UP && small_batch(a.T, a.K))
         return launch_k(k_expert_stream<DT, FLINT_ST_MB1S, FLINT_ST_NB1S, U, true>, grid, 256, lds, stream, m, a,
                         n_shared);
     if (GATE_UP)
@@ -330,12 +342,13 @@ static hipError_t launch_u(int U, const ExpertArgs &a, int grid, int n_shared, s
 template <typename DT>
 static hipError_t launch_stream_t(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
-    const int bm1 = stream_bm1(a.T), bm2 = FLINT_ST_MB2 * 16;
-    const int bn1 = (small_batch(a.T) ? FLINT_ST_NB1S : FLINT_ST_NB1) / 2 * 16, bn2 = FLINT_ST_NB2 * 16;
+    const int bm1 = stream_bm1(a.T, a.K), bm2 = FLINT_ST_MB2 * 16;
+    const int bn1 = (small_batch(a.T, a.K) ? FLINT_ST_NB1S : FLINT_ST_NB1) / 2 * 16, bn2 = FLINT_ST_NB2 * 16;
     const int cap1 = list_capacity(a.T, a.K, a.E, bm1);
     const int cap2 = list_capacity(a.T, a.K, a.E, bm2);
     const int ns1 = a.Is > 0 ? (a.T + bm1 - 1) / bm1 * (a.Is / bn1) : 0;
-    const int ns2 = a.Is > 0 ? (a.T + bm2 - 1) / bm2 * ((a.H + bn2 - 1) / bn2) : 0;
+    const int nsplit = a.shared_splits > 1 ? a.shared_splits : 1;
+    const int ns2 = a.Is > 0 ? (a.T + bm2 - 1) / bm2 * ((a.H + bn2 - 1) / bn2) * nsplit : 0;
     const int max1 = ns1 + cap1 * (a.I / bn1);
     const int max2 = ns2 + cap2 * ((a.H + bn2 - 1) / bn2);
     const size_t lds1 = (size_t)(2 * cap1 + a.E + 1) * 4;
@@ -343,7 +356,7 @@ static hipError_t launch_stream_t(const ExpertArgs &a, hipStream_t stream, const
     const hipError_t err = launch_u<DT, true>(unroll_gate_up(a.H), a, min(FLINT_ST_WGS1 * a.cus, max1), ns1, lds1, stream,
                                               marks ? marks[0] : Marks{});
     if (err != hipSuccess) return err;
-    return launch_u<DT, false>(unroll_down(a.I, a.Is), a, min(FLINT_ST_WGS2 * a.cus, max2), ns2, lds2, stream,
+    return launch_u<DT, false>(unroll_down(a.I, a.Is / nsplit), a, min(FLINT_ST_WGS2 * a.cus, max2), ns2, lds2, stream,
                                marks ? marks[1] : Marks{});
 }
 
