@@ -347,7 +347,8 @@ DENSE_CASES = [
     ("d_t7_f32",    7,    128,  64,   False),
     ("d_t600",      600,  256,  512,  True),    # large-batch (tiled) kernels
     ("d_t700_f32",  700,  128,  128,  False),   # float32 large-batch kernels
-    ("d_flint32",   32,   2048, 6144, True),    # the dense layer's width, decode batch
+    ("d_flint32",   32,   2048, 6144, True),    # the dense layer's width, decode batch (down split 8 ways)
+    ("d_t20_s6",    20,   1024, 1536, True),    # down split 6 ways
 ]
 
 
@@ -385,8 +386,10 @@ def test_dense_every_token(case):
     assert torch.equal(out.view(torch.int32), again.view(torch.int32))  # deterministic
 
 
-def test_dense_bf16_output():
-    wl = inputs.custom("d_bf16out", 45, 256, 0, 0, 384, 0, True, seed=2, dense=True)
+@pytest.mark.parametrize("shape", [(45, 256, 384), (24, 1024, 1536)])  # one combine input; six partial sums
+def test_dense_bf16_output(shape):
+    T, H, I = shape
+    wl = inputs.custom("d_bf16out", T, H, 0, 0, I, 0, True, seed=2, dense=True)
     w, x = _dense(wl)
     _dense_check(wl, w, x, out_dtype=torch.bfloat16)
 
