@@ -24,7 +24,7 @@
 #define FLINT_TOPK_WAVE_T 4096  // largest batch selected one token per wave (16 lanes per token above)
 #endif
 #ifndef FLINT_TOPK_WAVE
-#define FLINT_TOPK_WAVE 1  // T <= 1024: bitwise K-th-largest search (1) or sorted-list merges (0)
+#define FLINT_TOPK_WAVE 1  // up to FLINT_TOPK_WAVE_T: bitwise K-th-largest search (1) or sorted-list merges (0)
 #endif
 
 #include "gemm_core.hpp"

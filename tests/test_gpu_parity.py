@@ -186,7 +186,7 @@ def test_route_entry_point_matches_forward_routing():
     assert torch.equal(idx, idx2) and torch.equal(tw, tw2)
 
 
-@pytest.mark.parametrize("T", [37, 1500])  # one wave per token (T <= 1024), 16-lane groups above
+@pytest.mark.parametrize("T", [37, 1500, 4100])  # one wave per token (T <= 4096), 16-lane groups above
 def test_route_exact_ties_go_to_the_lower_index(T):
     """Router rows in groups of four identical rows, group g scaled by (1 + g):
     the four experts of a group get equal float32 scores on both sides, so with
