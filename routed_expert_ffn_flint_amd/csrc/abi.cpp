@@ -416,6 +416,8 @@ flint_status check_dense(const flint_dense_dims *d, int32_t T)
 // reduction is split into `dense_splits` partial arrays that the combine adds.
 int dense_splits(const flint_dense_dims *d, int32_t T)
 {
+    if (expert_tiles_for(T, d->hidden, 1, 0, 0, d->inter, d->dtype == FLINT_BF16).tiled)
+        return tiled_dense_splits(T, d->hidden, d->inter);
     if (T > kStreamMaxT || !stream_eligible(T, d->hidden, 0, d->inter)) return 1;
     int best = 1;
     for (int s = 2; s <= 8; ++s)  // whole, even batches of 32-wide slices per wave in every split

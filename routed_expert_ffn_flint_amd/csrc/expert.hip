@@ -315,7 +315,7 @@ ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf1
     // tile holds every row an expert gets and each weight is read once.
     if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};
     if (tiled_eligible(T, K, E, H, I, Is, bf16))
-        return ExpertTiles{tiled_bm1(T, K, E), 0, tiled_bm2(T, K, E), 0, false, false, true};
+        return ExpertTiles{tiled_bm1(T, K, E, Is), 0, tiled_bm2(T, K, E), 0, false, false, true};
     return ExpertTiles{128, 64, 128, 128, false, false, false};
 }
 

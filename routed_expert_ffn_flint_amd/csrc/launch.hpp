@@ -168,10 +168,13 @@ hipError_t launch_experts_mx4(const ExpertArgs &a, hipStream_t stream, const Mar
 
 // LDS-tiled kernels for large bf16 batches: rows per gate/up and per down tile
 // (128 or 256, from the mean rows per expert), eligibility, launch.
-int tiled_bm1(int T, int K, int E);
+int tiled_bm1(int T, int K, int E, int Is);
 int tiled_bm2(int T, int K, int E);
 bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16);
 hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
+// Partial arrays the down product of a dense layer (K = 0) splits its
+// reduction into on the tiled kernels.
+int tiled_dense_splits(int T, int H, int Is);
 // The router product on the same tiles (large bf16 batches).
 bool tiled_router_eligible(int T, int H, bool bf16);
 #ifndef FLINT_ROUTER_SPLITS

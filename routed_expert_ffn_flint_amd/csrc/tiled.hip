@@ -34,7 +34,11 @@
 //   - work items are (expert tile, n-tile) with n fastest; XCD j runs the j-th
 //     eighth of the items, in order, so the n-tiles of one expert tile (which
 //     gather the same rows) and consecutive expert tiles (same weights) share
-//     that XCD's L2.
+//     that XCD's L2.  Shared-weight items (the shared expert, the dense layer)
+//     go n-tile outer over groups of 8 row tiles, so that both operands repeat
+//     in L2 (dense T = 4096 gate/up: 251 -> 235 us; its L2 misses had been
+//     14x the algorithmic bytes).  The down product deals each XCD an eighth
+//     of the shared and an eighth of the routed items.
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
@@ -43,6 +47,10 @@ namespace flint {
 namespace {
 
 constexpr int kXcds = 8;
+#ifndef FLINT_TL_GROUP
+#define FLINT_TL_GROUP 8
+#endif
+constexpr int kRowGroup = FLINT_TL_GROUP;  // row tiles per group of shared-weight items
 constexpr int kLdsBytes = 160 * 1024;
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
@@ -104,6 +112,24 @@ __device__ __forceinline__ int xcd_item(int total)
     return (slot < per && item < total) ? item : -1;
 }
 
+// The same for a launch of ns shared-weight items followed by nr routed ones:
+// each XCD takes an eighth of each kind (shared items first), so a kind whose
+// items are longer (a wider shared expert) loads every XCD alike (T = 16384
+// down product: 604 -> 481 us).  The grid holds 8 * (ceil(ns / 8) +
+// ceil(routed capacity / 8)) work-groups.
+__device__ __forceinline__ int xcd_item2(int ns, int nr)
+{
+    const int ps = (ns + kXcds - 1) / kXcds, pr = (nr + kXcds - 1) / kXcds;
+    const int x = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    if (slot < ps) {
+        const int item = x * ps + slot;
+        return item < ns ? item : -1;
+    }
+    const int s2 = slot - ps;
+    const int r = x * pr + s2;
+    return (s2 < pr && r < nr) ? ns + r : -1;
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others at their "no wait" maximum).
 template <int N>
@@ -153,10 +179,12 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
     const int H = a.H;
 
     // ---- the work item: rows [row0, row_end) of A, n-tile nt, reduction kdim
+    // from kbase of rows kstride long
     int row0, row_end, nt, kdim, e = 0;
     bool shared = false;
-    int kbase = 0;  // ROUTER: first k of this split
+    int kbase = 0, kstride = 0;
     float *lout = nullptr;
+    float *yout = nullptr;  // DOWN: the output array of this item
     if (MODE == ROUTER) {
         const int ntn = (a.E + BN - 1) / BN;
         const int item = xcd_item(((a.T + BM - 1) / BM) * ntn * ta.ksplit);
@@ -167,20 +195,37 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
         row_end = a.T;
         kdim = H / ta.ksplit;
         kbase = ks * kdim;
+        kstride = H;
         lout = ta.logits + (size_t)ks * a.T * a.E;
         if (ks != 0) ta.bias = nullptr;
     } else {
         const int ntn_shared = MODE == GATE_UP ? a.Is / (BN / 2) : (H + BN - 1) / BN;
         const int ntn_routed = MODE == GATE_UP ? a.I / (BN / 2) : (H + BN - 1) / BN;
         const int nlist = MODE == GATE_UP ? (a.K > 0 ? a.meta[0] : 0) : (a.K > 0 ? a.meta[1] : 0);
-        const int item = xcd_item(ta.n_shared + nlist * ntn_routed);
+        // gate/up: all items cost alike, and contiguous eighths keep the shared
+        // expert's weights on one XCD; down: shared items reduce over Is, routed
+        // ones over I, so each XCD takes its share of both kinds
+        const int item = MODE == GATE_UP ? xcd_item(ta.n_shared + nlist * ntn_routed)
+                                         : xcd_item2(ta.n_shared, nlist * ntn_routed);
         if (item < 0) return;
         shared = item < ta.n_shared;
         if (shared) {
-            row0 = (item / ntn_shared) * BM;
-            nt = item % ntn_shared;
+            // down: split sp of the reduction over Is (split outermost)
+            const int nrt = (a.T + BM - 1) / BM;
+            const int sp = MODE == DOWN ? item / (nrt * ntn_shared) : 0;
+            const int it = MODE == DOWN ? item % (nrt * ntn_shared) : item;
+            // groups of kRowGroup row tiles, n-tile outer within a group: the
+            // work-groups running together on an XCD cover a few row tiles and a
+            // few n-tiles, and both their rows and their weights repeat in L2
+            const int g = it / (kRowGroup * ntn_shared), w = it % (kRowGroup * ntn_shared);
+            const int rows_here = min(kRowGroup, nrt - g * kRowGroup);
+            row0 = (g * kRowGroup + w % rows_here) * BM;
+            nt = w / rows_here;
             row_end = a.T;
-            kdim = MODE == GATE_UP ? H : a.Is;
+            kstride = MODE == GATE_UP ? H : a.Is;
+            kdim = MODE == GATE_UP ? H : a.Is / (a.shared_splits > 1 ? a.shared_splits : 1);
+            kbase = sp * kdim;
+            yout = a.y_shared + (size_t)sp * a.T * H;
         } else {
             const int r = item - ta.n_shared;
             const int entry = r / ntn_routed;
@@ -189,7 +234,8 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
             row0 = list[2 * entry + 1];
             nt = r % ntn_routed;
             row_end = a.offsets[e + 1];
-            kdim = MODE == GATE_UP ? H : a.I;
+            kdim = kstride = MODE == GATE_UP ? H : a.I;
+            yout = a.y_sorted;
         }
     }
 
@@ -209,7 +255,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
             const int tok = shared ? r : a.sorted_token[r];
             ga[i] = (const S *)a.x + (size_t)tok * H + chunk;
         } else if (MODE == DOWN) {
-            ga[i] = (shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * kdim + chunk;
+            ga[i] = (shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * kstride + kbase + chunk;
         } else {
             ga[i] = (const S *)a.x + (size_t)r * H + kbase + chunk;
         }
@@ -229,7 +275,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
             int c = nt * BN + rr;
             if (c >= H) c = 0;
             const S *w = shared ? (const S *)a.shared_down : (const S *)a.down + (size_t)e * H * a.I;
-            gb[i] = w + (size_t)c * kdim + chunk;
+            gb[i] = w + (size_t)c * kstride + kbase + chunk;
         } else {
             int c = nt * BN + rr;
             if (c >= a.E) c = 0;
@@ -375,7 +421,6 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
                     hout[(size_t)r * width + ch] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + NB / 2][i]));
                 }
             } else if (MODE == DOWN) {
-                float *yout = shared ? a.y_shared : a.y_sorted;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int c = nt * BN + wn * C::WN + j * 16 + (lane & 15);
@@ -421,8 +466,32 @@ int cfg_bm(int which) { return which >= 1 && which <= 3 ? 256 : 128; }
 int cfg_bn(int which) { return which >= 2 ? 256 : 128; }
 
 bool big_batch(int T, int K, int E) { return (long long)T * K >= (long long)FLINT_TL_BIG_ROWS * E; }
-int gu_cfg(int T, int K, int E) { return big_batch(T, K, E) ? FLINT_TL_GU_BIG : FLINT_TL_GU_SMALL; }
-int dn_cfg(int T, int K, int E) { return big_batch(T, K, E) ? FLINT_TL_DN_BIG : FLINT_TL_DN_SMALL; }
+
+// A dense layer (no routed experts) has T rows in every product, so its tiles
+// come in whole waves over the 256 CUs of an MI355X (one work-group per CU
+// for the 128 x 256 and 256 x 256 tiles).  Gate/up takes the 256 x 256 tiles
+// (twice the work per item) when their waves cost no more than the 128 x 256
+// tiles' waves, which picks the faster of the two at every T measured
+// (640 ... 8192 rows, width 6144: small below 1024 and for 1536 ... 3072).
+// The down product always takes them and splits its reduction to fill the
+// CUs (see tiled_dense_splits).
+constexpr int kDenseCus = 256;
+bool dense_gu_big(int T, int Is)
+{
+    const long long n = Is / 128;  // 128-channel gate + up column tiles
+    const long long big = (T + 255) / 256 * n, small = (T + 127) / 128 * n;
+    return 2 * ((big + kDenseCus - 1) / kDenseCus) <= (small + kDenseCus - 1) / kDenseCus;
+}
+int gu_cfg(int T, int K, int E, int Is)
+{
+    if (K == 0) return Is % 128 == 0 && dense_gu_big(T, Is) ? 3 : FLINT_TL_GU_SMALL;
+    return big_batch(T, K, E) ? FLINT_TL_GU_BIG : FLINT_TL_GU_SMALL;
+}
+int dn_cfg(int T, int K, int E)
+{
+    if (K == 0) return 3;
+    return big_batch(T, K, E) ? FLINT_TL_DN_BIG : FLINT_TL_DN_SMALL;
+}
 
 template <int MODE, typename C>
 hipError_t launch_cfg(TiledArgs ta, hipStream_t stream, Marks m)
@@ -435,8 +504,8 @@ hipError_t launch_cfg(TiledArgs ta, hipStream_t stream, Marks m)
     } else {
         const int ntn_s = MODE == GATE_UP ? a.Is / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
         const int ntn_r = MODE == GATE_UP ? a.I / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
-        ta.n_shared = a.Is > 0 ? mt * ntn_s : 0;
-        items = ta.n_shared + list_capacity(a.T, a.K, a.E, C::BM) * ntn_r;
+        ta.n_shared = a.Is > 0 ? mt * ntn_s * (MODE == DOWN && a.shared_splits > 1 ? a.shared_splits : 1) : 0;
+        items = (ta.n_shared + kXcds - 1) / kXcds * kXcds + list_capacity(a.T, a.K, a.E, C::BM) * ntn_r;
     }
     const int grid = (items + kXcds - 1) / kXcds * kXcds;
     return launch_k(k_tiled<MODE, C>, grid, C::THREADS, 0, stream, m, ta);
@@ -463,19 +532,34 @@ bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16)
 {
     // whole k slices (H, I, Is); a gate/up tile takes BN/2 gate channels and
     // the same up channels
-    const int which = gu_cfg(T, K, E);
+    const int which = gu_cfg(T, K, E, Is);
     const int half = cfg_bn(which == 6 ? 0 : which) / 2;  // CfgWideN falls back to CfgSmall
     return bf16 && H % 64 == 0 && I % 64 == 0 && Is % 64 == 0 && I % half == 0 && Is % half == 0;
 }
 
-int tiled_bm1(int T, int K, int E) { return cfg_bm(gu_cfg(T, K, E)); }
+// The dense down product on 256 x 256 tiles reduces over the whole width,
+// with few tiles for moderate T (T = 4096, H = 2048: 128 tiles on 256 CUs).
+// It is split into the most partial arrays (a power of two up to 8, each a
+// whole number of 64-wide slices) that keep the items within one wave; the
+// combine adds them.  Measured (H = 2048, width 6144, layer time): T = 640
+// 112 -> 85 us (8 splits), 2048 225 -> 202 (4), 3072 347 -> 293 (2), 4096
+// 349 -> 342 (2); at 8192 one split (256 tiles) is best.
+int tiled_dense_splits(int T, int H, int Is)
+{
+    const long long tiles = (long long)(T + 255) / 256 * ((H + 255) / 256);
+    int s = 1;
+    while (s < 8 && tiles * (2 * s) <= kDenseCus && Is % (64 * 2 * s) == 0) s *= 2;
+    return s;
+}
+
+int tiled_bm1(int T, int K, int E, int Is) { return cfg_bm(gu_cfg(T, K, E, Is)); }
 int tiled_bm2(int T, int K, int E) { return cfg_bm(dn_cfg(T, K, E)); }
 
 hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
     TiledArgs ta{};
     ta.e = a;
-    const hipError_t err = launch_mode<GATE_UP>(gu_cfg(a.T, a.K, a.E), ta, stream, marks ? marks[0] : Marks{});
+    const hipError_t err = launch_mode<GATE_UP>(gu_cfg(a.T, a.K, a.E, a.Is), ta, stream, marks ? marks[0] : Marks{});
     if (err != hipSuccess) return err;
     return launch_mode<DOWN>(dn_cfg(a.T, a.K, a.E), ta, stream, marks ? marks[1] : Marks{});
 }

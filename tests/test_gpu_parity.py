@@ -345,7 +345,8 @@ DENSE_CASES = [
     ("d_t1",        1,    128,  192,  True),
     ("d_t33",       33,   256,  320,  True),
     ("d_t7_f32",    7,    128,  64,   False),
-    ("d_t600",      600,  256,  512,  True),    # large-batch (tiled) kernels
+    ("d_t600",      600,  256,  512,  True),    # large-batch (tiled) kernels, down split 8 ways
+    ("d_t1000",     1000, 256,  6144, True),    # 256 x 256 gate/up tiles, ragged last tile
     ("d_t700_f32",  700,  128,  128,  False),   # float32 large-batch kernels
     ("d_flint32",   32,   2048, 6144, True),    # the dense layer's width, decode batch (down split 8 ways)
     ("d_t20_s6",    20,   1024, 1536, True),    # down split 6 ways
