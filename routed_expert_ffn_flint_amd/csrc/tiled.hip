@@ -83,6 +83,9 @@ struct Cfg {
 #ifndef FLINT_TL_ROTATE
 #define FLINT_TL_ROTATE 1
 #endif
+#ifndef FLINT_TL_SKIP_DEAD
+#define FLINT_TL_SKIP_DEAD 1
+#endif
 #ifndef FLINT_TL_S_BK
 #define FLINT_TL_S_BK 32
 #endif
@@ -359,11 +362,16 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
         return (s >= nk ? s - nk : s) * BK;
     };
     Frags fr[2];
-    // j: position in the unrolled round (stage j % STAGES)
-    auto step = [&](int j, int q, int kt) {
+    // j: position in the unrolled round (stage j % STAGES).  LIVE: the wave
+    // has rows to compute.  A wave whose rows are all padding (the second half
+    // of an expert's last tile when at most WM rows are left) only fetches its
+    // share of the slices and keeps the barriers, so the MFMA pipes serve the
+    // live waves alone.
+    auto step = [&](auto live, int j, int q, int kt) {
+        constexpr bool LIVE = decltype(live)::value;
         const int p = (j * C::NQ + q) & 1;
         const int st = j % STAGES;
-        wait_lds();  // fr[p] has landed
+        if (LIVE) wait_lds();  // fr[p] has landed
         __builtin_amdgcn_sched_barrier(0);
         if (q == C::NQ - 1) {
             wait_vmcnt<(STAGES - 3) * kLoadsPerSlice>();
@@ -371,35 +379,47 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
             __builtin_amdgcn_sched_barrier(0);
             fetch(stage((st + STAGES - 1) % STAGES), kofs(kt + STAGES - 1));
             __builtin_amdgcn_sched_barrier(0);
-            read(fr[p ^ 1], stage((st + 1) % STAGES), 0);
-        } else {
+            if (LIVE) read(fr[p ^ 1], stage((st + 1) % STAGES), 0);
+        } else if (LIVE) {
             read(fr[p ^ 1], stage(st), q + 1);
         }
-        mmas(fr[p]);
-        interleave();
+        if (LIVE) {
+            mmas(fr[p]);
+            interleave();
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
+    auto run = [&](auto live) {
 #pragma unroll
-    for (int s = 0; s + 1 < STAGES; ++s) fetch(stage(s), kofs(s));
-    wait_vmcnt<(STAGES - 2) * kLoadsPerSlice>();
-    __builtin_amdgcn_s_barrier();
-    read(fr[0], stage(0), 0);
-    // whole rounds, with no branch inside (so the compiler keeps its own waits
-    // off the LDS reads); then the rest
-    constexpr int ROUND = C::ROUND;
-    const int nfull = nk / ROUND * ROUND;
-    for (int kb = 0; kb < nfull; kb += ROUND) {
+        for (int s = 0; s + 1 < STAGES; ++s) fetch(stage(s), kofs(s));
+        wait_vmcnt<(STAGES - 2) * kLoadsPerSlice>();
+        __builtin_amdgcn_s_barrier();
+        if (decltype(live)::value) read(fr[0], stage(0), 0);
+        // whole rounds, with no branch inside (so the compiler keeps its own
+        // waits off the LDS reads); then the rest
+        constexpr int ROUND = C::ROUND;
+        const int nfull = nk / ROUND * ROUND;
+        for (int kb = 0; kb < nfull; kb += ROUND) {
 #pragma unroll
-        for (int j = 0; j < ROUND; ++j)
+            for (int j = 0; j < ROUND; ++j)
 #pragma unroll
-            for (int q = 0; q < C::NQ; ++q) step(j, q, kb + j);
-    }
+                for (int q = 0; q < C::NQ; ++q) step(live, j, q, kb + j);
+        }
 #pragma unroll
-    for (int j = 0; j + 1 < ROUND; ++j) {
-        if (nfull + j >= nk) break;
+        for (int j = 0; j + 1 < ROUND; ++j) {
+            if (nfull + j >= nk) break;
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q) step(j, q, nfull + j);
-    }
+            for (int q = 0; q < C::NQ; ++q) step(live, j, q, nfull + j);
+        }
+    };
+#if FLINT_TL_SKIP_DEAD
+    if (row0 + wm * C::WM < row_end)
+        run(std::integral_constant<bool, true>{});
+    else
+        run(std::integral_constant<bool, false>{});
+#else
+    run(std::integral_constant<bool, true>{});
+#endif
     // no load may still be writing this work-group's LDS when it exits
     wait_vmcnt<0>();
     wait_lds();
