@@ -12,8 +12,9 @@ workloads rotate through several independently drawn weight copies so that the
 last-level cache cannot serve repeated weight reads.
 
 Prints ONE JSON line.  Beside the headline throughput:
-  roofline      the dominant kernel's algorithmic bytes (or flops) per launch
-                over its mean launch duration, from HIP events that the library
+  roofline      the dominant kernel's algorithmic bytes per launch (flops when
+                its flop per byte exceed the ridge point, 2.5 PFLOP/s over
+                8 TB/s) over its mean launch duration, from HIP events that the library
                 stamps at that kernel's own begin and end (hipExtLaunchKernel,
                 on the library's stream) during a second pass of the same
                 steps, against MI355X's published peak; `traffic` is the HBM
@@ -39,6 +40,8 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# flop per byte above which a kernel is bound by the matrix cores, not by HBM
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 METRIC = "MoE-layer tokens/s (bf16, H=2048, 256e top-6) + % HBM/MFMA roofline"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "routed_expert_ffn_flint_amd", "csrc")
@@ -242,7 +245,7 @@ def bench_dense(args, wl):
     gu_flops = 4 * T * I * H
     layer_bytes = 3 * I * H * eb + T * H * eb + T * H * 4
     layer_flops = 6 * T * I * H
-    big = T >= 2048
+    big = gu_flops / gu_bytes >= RIDGE  # arithmetic intensity of the gate/up kernel
     kernel = "k_expert_stream" if T <= STREAM_MAX_T else "k_tiled"
     digest = sources_digest(kernel)
     kname = f"{kernel}<gate/up> (gate/up GEMM + SwiGLU of the dense layer)"
@@ -449,7 +452,7 @@ def main():
     layer_bytes = avg("layer_bytes")
     layer_flops = float(np.mean([p["flops"]["layer"] for p in per_copy]))
     gu_flops = float(np.mean([p["flops"]["gate_up"] for p in per_copy]))
-    big = T >= 2048
+    big = gu_flops / gate_up_bytes >= RIDGE  # arithmetic intensity of the gate/up kernel
     kernel = ("k_expert_stream_mx4" if wl.mx4 else "k_expert_stream") if T <= STREAM_MAX_T else "k_tiled"
     digest = sources_digest(kernel)
     traffic = counters_traffic(kernel, wl.name, digest)
