@@ -14,14 +14,16 @@ last-level cache cannot serve repeated weight reads.
 Prints ONE JSON line.  Beside the headline throughput:
   roofline      the dominant kernel's algorithmic bytes per launch (flops when
                 its flop per byte exceed the ridge point, 2.5 PFLOP/s over
-                8 TB/s) over its mean launch duration, from HIP events that the library
-                stamps at that kernel's own begin and end (hipExtLaunchKernel,
+                8 TB/s) over its mean launch duration, from HIP events that
+                the library stamps at that kernel's own begin and end (hipExtLaunchKernel,
                 on the library's stream) during a second pass of the same
                 steps, against MI355X's published peak; `traffic` is the HBM
                 bytes per launch that the committed rocprofv3 counter summary
                 for this kernel and workload records (FETCH_SIZE + WRITE_SIZE,
                 scaled by the same counters on a plain copy), or null when the
                 kernel's sources have changed since it was taken;
+  step_us_percentiles  p10 / median / p90 of single steps (a third pass,
+                an event pair around each step);
   cpu_baseline  the oracle (plain fp64 C) timed on the host on a bounded
                 sample of the same workload.
 """
@@ -111,6 +113,22 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(e)
+
+
+def step_percentiles(step, n):
+    """p10 / median / p90 of single steps, microseconds: a further pass of n
+    steps, each between two events on the library's stream."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs], dtype=np.float64)
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"p10": float(p10), "p50": float(p50), "p90": float(p90), "steps": n}
 
 
 def sources_digest(kernel):
@@ -275,6 +293,7 @@ def bench_dense(args, wl):
                            "mfma_frac": layer_flops / lt / 1e12 / BF16_PEAK_TFLOPS,
                            "algorithmic_bytes": layer_bytes, "flops": layer_flops},
         "stages_us": stage_us,
+        "step_us_percentiles": step_percentiles(step, n_prof),
     }
     if not args.no_cpu_baseline:
         from oracle import oracle as orc
@@ -489,6 +508,7 @@ def main():
         "roofline": roofline,
         "layer_roofline": layer,
         "stages_us": stage_us,
+        "step_us_percentiles": step_percentiles(step, n_prof),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layers[0], x, args.cpu_seconds)

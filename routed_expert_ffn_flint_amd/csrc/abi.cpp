@@ -93,7 +93,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
         off += align_up(bytes ? bytes : 1);
         return p;
     };
-    w.logits = (float *)take((size_t)router_splits(T, H, eb == 2) * T * E * 4);
+    w.logits = (float *)take((size_t)router_splits(T, H, E, eb == 2) * T * E * 4);
     w.hist = (int32_t *)take((size_t)ntiles * E * 4);
     w.tile_base = (int32_t *)take((size_t)ntiles * E * 4);
     w.rank = (int32_t *)take(TK * 4);
@@ -171,7 +171,7 @@ flint_status flint_moe_route(const flint_moe_dims *d, int32_t T, const void *x, 
     a.E = d->n_experts;
     a.K = d->top_k;
     a.logits = w.logits;
-    a.logit_splits = router_splits(T, d->hidden, d->dtype == FLINT_BF16);
+    a.logit_splits = router_splits(T, d->hidden, d->n_experts, d->dtype == FLINT_BF16);
     a.topk_idx = topk_idx;
     a.topk_w = topk_w;
     a.compute_topk = true;
@@ -271,7 +271,7 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
         a.bm2 = mx4_bm2();
     }
     a.logits = w.logits;
-    a.logit_splits = router_splits(T, d->hidden, bf16);
+    a.logit_splits = router_splits(T, d->hidden, d->n_experts, bf16);
     a.topk_idx = topk_idx_out ? topk_idx_out : w.topk_idx;
     a.topk_w = topk_w_out ? topk_w_out : w.topk_w;
     a.compute_topk = true;

@@ -98,8 +98,11 @@ int device_cus();
 // ---- launches (all enqueue on `stream`, return hipGetLastError()) ----------
 
 // Number of partial logit arrays the router writes (the sum over slices of H
-// is split for large batches); the top-k kernels add them in order.
-int router_splits(int T, int H, bool bf16);
+// is split for batches of 1024-4096 tokens, and below 1024 when the batch has
+// few router tiles); the top-k kernels add them in order.
+int router_splits(int T, int H, int E, bool bf16);
+// Partial arrays of the router product for T < 1024 (work-groups per 16x16 tile).
+int small_router_splits(int T, int H, int E);
 
 // logits[t][e] = x[t] . router[e] (+ bias[e]), float32, as router_splits
 // partial arrays (bias in the first) that sum to it.

@@ -589,7 +589,11 @@ bool tiled_router_eligible(int T, int H, bool bf16) { return bf16 && T >= 1024 &
 // Split the sum over H while the batch alone gives too few tiles to fill the
 // chip (measured: faster up to 4096 tokens; at 16384 the extra partial
 // arrays cost more than they save).
-int router_splits(int T, int H, bool bf16) { return tiled_router_eligible(T, H, bf16) && T <= 4096 ? kRouterSplits : 1; }
+int router_splits(int T, int H, int E, bool bf16)
+{
+    if (T < 1024) return small_router_splits(T, H, E);
+    return tiled_router_eligible(T, H, bf16) && T <= 4096 ? kRouterSplits : 1;
+}
 
 hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
                                float *logits, hipStream_t stream, Marks m)
@@ -602,7 +606,7 @@ hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, 
     ta.router = router;
     ta.bias = bias;
     ta.logits = logits;
-    ta.ksplit = router_splits(T, H, true);
+    ta.ksplit = router_splits(T, H, E, true);
     return launch_mode<ROUTER>(FLINT_TL_ROUTER, ta, stream, m);
 }
 
