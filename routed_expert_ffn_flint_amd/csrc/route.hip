@@ -154,42 +154,51 @@ hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const vo
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive scan of one int per thread over the first 256 threads
-// (threads beyond 256 contribute 0).  Every thread of the block must call it.
-__device__ int block_exclusive_scan256(int v, int *lds8, int *total)
+// Block-wide exclusive scans of three ints per thread over the first 256
+// threads (threads beyond 256 contribute 0), with two barriers for all three.
+// Every thread of the block must call it; lds holds 12 ints.
+__device__ void block_exclusive_scan256x3(const int (&v)[3], int *lds, int (&excl)[3], int (&total)[3])
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x >= 256) v = 0;
-    int incl = v;
+    int incl[3];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
+    for (int j = 0; j < 3; ++j) incl[j] = threadIdx.x < 256 ? v[j] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int y = __shfl_up(incl[j], off, 64);
+            if (lane >= off) incl[j] += y;
+        }
+    if (lane == 63 && wave < 4)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) lds[4 * j + wave] = incl[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        int base = 0;
+        for (int w = 0; w < 4 && w < wave; ++w) base += lds[4 * j + w];
+        total[j] = lds[4 * j] + lds[4 * j + 1] + lds[4 * j + 2] + lds[4 * j + 3];
+        excl[j] = base + incl[j] - (threadIdx.x < 256 ? v[j] : 0);
     }
-    if (lane == 63 && wave < 4) lds8[wave] = incl;
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < 4 && w < wave; ++w) base += lds8[w];
-    *total = lds8[0] + lds8[1] + lds8[2] + lds8[3];
-    __syncthreads();
-    return base + incl - v;
 }
 
 // Counts -> offsets and the expert kernels' tile lists.  Thread e < E holds
 // counts[e] in `c`.  lists: entry i = (expert, first slot of the tile).
-__device__ void finish_offsets_and_lists(int c, int E, int32_t *offsets, int32_t *counts,
-                                         int32_t *list1, int bm1, int32_t *list2, int bm2,
-                                         int32_t *meta, int *lds8)
+__device__ int finish_offsets_and_lists(int c, int E, int32_t *offsets, int32_t *counts,
+                                        int32_t *list1, int bm1, int32_t *list2, int bm2,
+                                        int32_t *meta, int *lds)
 {
     const int e = threadIdx.x;
     const bool own = e < E;
     if (!own) c = 0;
-    int total;
-    const int off = block_exclusive_scan256(c, lds8, &total);
-    const int n1 = (c + bm1 - 1) / bm1, n2 = (c + bm2 - 1) / bm2;
-    int tot1, tot2;
-    const int st1 = block_exclusive_scan256(n1, lds8, &tot1);
-    const int st2 = block_exclusive_scan256(n2, lds8, &tot2);
+    // slots, gate/up tiles and down tiles of each expert
+    const int n[3] = {c, (c + bm1 - 1) / bm1, (c + bm2 - 1) / bm2};
+    int ex[3], tot[3];
+    block_exclusive_scan256x3(n, lds, ex, tot);
+    const int off = ex[0], total = tot[0], n1 = n[1], n2 = n[2], st1 = ex[1], st2 = ex[2];
+    const int tot1 = tot[1], tot2 = tot[2];
     if (own) {
         counts[e] = c;
         offsets[e] = off;
@@ -207,6 +216,7 @@ __device__ void finish_offsets_and_lists(int c, int E, int32_t *offsets, int32_t
         meta[0] = tot1;
         meta[1] = tot2;
     }
+    return off;  // expert threadIdx.x's first slot
 }
 
 __device__ __forceinline__ float score_from_logit(float z)
@@ -302,7 +312,7 @@ struct TileLds {
     int16_t sel[kTopkTile * kMaxTopK];
     uint32_t masks[kMaxExperts * (kTopkTile / 32)];
     int32_t offs[kMaxExperts];
-    int lds8[8];
+    int lds[12];
 };
 
 // Dispatch of one tile of up to 256 tokens by a work-group of NT threads: a
@@ -356,8 +366,9 @@ __device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, Tile
         if (threadIdx.x < E) a.hist[(size_t)tile * E + threadIdx.x] = hcount;
         return;
     }
-    finish_offsets_and_lists(hcount, E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2, a.meta, L.lds8);
-    if (threadIdx.x < E) L.offs[threadIdx.x] = a.offsets[threadIdx.x];  // this thread's own write
+    const int off = finish_offsets_and_lists(hcount, E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2,
+                                             a.meta, L.lds);
+    if (threadIdx.x < E) L.offs[threadIdx.x] = off;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
@@ -412,7 +423,8 @@ __device__ __forceinline__ void write_topk(const uint64_t (&l)[kMaxTopK], int t,
 // are >= 0, so their bit patterns order like the values, and the K-th largest
 // pattern is the largest v with at least K patterns >= v, found one bit at a
 // time from the top with wave-wide counts (ballots).  Then every score above
-// it is selected, and of those equal to it the lowest expert indices up to K.
+// it is selected, and of those equal to it the lowest expert indices up to K
+// (with an early stop, the prefix found instead: see below).
 // A chain of ~32 short compare/count steps instead of log2(64) merges of
 // sorted 8-entry lists.  Writes topk_idx (ascending ids) and topk_w (s over
 // the sum of the K selected, the sum in double in ascending id order).
@@ -437,13 +449,19 @@ __device__ __forceinline__ void wave_topk(const float *zt, size_t split_stride, 
         for (int i = 0; i < 4; ++i) z[i] += zt[sp * split_stride + (v[i] ? lane + 64 * i : 0)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) u[i] = v[i] ? __float_as_uint(score_from_logit(z[i])) : 0u;
+    // (bit 31, the sign, is 0 in every score.)  Once exactly K patterns are
+    // >= the prefix, those K are the selection: the loop stops there (the
+    // count is wave-uniform), typically after half the bits.
     uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 30; bit >= 0; --bit) {
         const uint32_t cand = thr | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(v[i] && u[i] >= cand));
-        if (cnt >= K) thr = cand;
+        if (cnt >= K) {
+            thr = cand;
+            if (cnt == K) break;
+        }
     }
     int gt = 0;
 #pragma unroll
@@ -511,7 +529,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_tile(DispatchArgs a, int fuse
 // More than one tile: per-expert column scan of the tile histograms.
 __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a, int ntiles)
 {
-    __shared__ int lds8[8];
+    __shared__ int lds[12];
     const int e = threadIdx.x;
     int run = 0;
     if (e < a.E) {
@@ -527,7 +545,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a, int ntile
         }
     }
     finish_offsets_and_lists(run, a.E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2,
-                             a.meta, lds8);
+                             a.meta, lds);
 }
 
 __global__ __launch_bounds__(256) void k_dispatch_scatter(DispatchArgs a)
