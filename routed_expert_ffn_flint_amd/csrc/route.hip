@@ -23,6 +23,12 @@
 #ifndef FLINT_TOPK_WAVE_T
 #define FLINT_TOPK_WAVE_T 4096  // largest batch selected one token per wave (16 lanes per token above)
 #endif
+#ifndef FLINT_TOPK_FUSED_T
+// Largest batch whose top-k and dispatch run as one work-group of 16 waves,
+// one token per wave (T = 8: 10.2 -> 7.4 us; with two tokens per wave their
+// latencies add up: T = 32 9.8 -> 12.9 us).
+#define FLINT_TOPK_FUSED_T 16
+#endif
 #ifndef FLINT_TOPK_WAVE
 #define FLINT_TOPK_WAVE 1  // up to FLINT_TOPK_WAVE_T: bitwise K-th-largest search (1) or sorted-list merges (0)
 #endif
@@ -322,7 +328,7 @@ struct TileLds {
 // (`single`) the same work-group also scans the counts, scatters the
 // permutation and writes the expert kernels' tile lists.
 template <int NT>
-__device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, TileLds &L)
+__device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, TileLds &L, bool sel_in_lds)
 {
     constexpr int PER = kTopkTile * kMaxTopK / NT;  // pairs per thread, at most
     constexpr int W = kTopkTile / 32;
@@ -330,7 +336,8 @@ __device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, Tile
     const int t_base = tile * kTopkTile;
     const int tile_len = min(kTopkTile, a.T - t_base);
 
-    for (int i = threadIdx.x; i < tile_len * K; i += NT) L.sel[i] = (int16_t)a.topk_idx[(size_t)t_base * K + i];
+    if (!sel_in_lds)
+        for (int i = threadIdx.x; i < tile_len * K; i += NT) L.sel[i] = (int16_t)a.topk_idx[(size_t)t_base * K + i];
     for (int i = threadIdx.x; i < E * W; i += NT) L.masks[i] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < tile_len * K; i += NT) {
@@ -430,7 +437,7 @@ __device__ __forceinline__ void write_topk(const uint64_t (&l)[kMaxTopK], int t,
 // the sum of the K selected, the sum in double in ascending id order).
 __device__ __forceinline__ void wave_topk(const float *zt, size_t split_stride, int nsplit, int E, int K, int t,
                                           int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-                                          float *ls, int *le)
+                                          float *ls, int *le, int16_t *sel_lds = nullptr)
 {
     const int lane = threadIdx.x & 63;
     uint32_t u[4];
@@ -490,6 +497,7 @@ __device__ __forceinline__ void wave_topk(const float *zt, size_t split_stride, 
     if (lane < K) {
         topk_idx[(size_t)t * K + lane] = le[lane];
         topk_w[(size_t)t * K + lane] = (float)((double)ls[lane] / sum);
+        if (sel_lds) sel_lds[t * K + lane] = (int16_t)le[lane];  // (a one-tile batch: t is tile-relative)
     }
 }
 
@@ -523,7 +531,24 @@ __global__ __launch_bounds__(256) void k_topk(DispatchArgs da)
 __global__ __launch_bounds__(1024) void k_dispatch_tile(DispatchArgs a, int fused_single_tile)
 {
     __shared__ TileLds L;
-    dispatch_tile<1024>(a, blockIdx.x, fused_single_tile != 0, L);
+    dispatch_tile<1024>(a, blockIdx.x, fused_single_tile != 0, L, false);
+}
+
+// Small batches (up to 16 tokens): top-k (one token per wave, 16 waves) and
+// the whole dispatch in one work-group; the selection reaches the dispatch
+// through LDS.  One launch instead of two, and no round trip of topk_idx
+// through memory.
+__global__ __launch_bounds__(1024) void k_topk_dispatch_small(DispatchArgs a)
+{
+    __shared__ TileLds L;
+    __shared__ float ls[16][kMaxTopK];
+    __shared__ int le[16][kMaxTopK];
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < a.T; t += 16)
+        wave_topk(a.logits + (size_t)t * a.E, (size_t)a.T * a.E, a.logit_splits, a.E, a.K, t, a.topk_idx, a.topk_w,
+                  ls[wave], le[wave], L.sel);
+    __syncthreads();
+    dispatch_tile<1024>(a, 0, true, L, true);
 }
 
 // More than one tile: per-expert column scan of the tile histograms.
@@ -581,6 +606,8 @@ hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks
     // the first kernel carries m.start, the last m.stop
     Marks first{m.start, a.dispatch ? nullptr : m.stop};
     hipError_t err = hipSuccess;
+    if (a.compute_topk && a.dispatch && fused && a.T <= FLINT_TOPK_FUSED_T && FLINT_TOPK_WAVE && a.E <= 256)
+        return launch_k(k_topk_dispatch_small, 1, 1024, 0, stream, m, a);
     if (a.compute_topk) {
         err = a.T <= FLINT_TOPK_WAVE_T ? launch_k(FLINT_TOPK_WAVE ? k_topk_wave : k_topk<64>, (a.T + 3) / 4, 256, 0, stream, first, a)
                           : launch_k(k_topk<16>, (a.T + 15) / 16, 256, 0, stream, first, a);

@@ -86,11 +86,12 @@ def test_decode32_every_token():
           f"distinct experts={len(np.unique(st['idx']))}")
 
 
-@pytest.mark.parametrize("T", [1, 5, 33, 200, 512, 513])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 33, 200, 512, 513])
 def test_flint_layer_small_batches(T):
     """Flint-shaped layer (H=2048, 256 experts top-6, 512/1024 wide) at batch
     sizes around the decode kernels' range (up to 512 tokens; 513 takes the
-    tiled kernels): routing of every token, outputs of sampled tokens."""
+    tiled kernels; up to 16 tokens top-k and dispatch share one work-group):
+    routing of every token, outputs of sampled tokens."""
     wl = inputs.Workload(f"flint_T{T}", T, 2048, 256, 6, 512, 1024, True, 5)
     w, x = _layer(wl)
     sample = list(range(T)) if T <= 40 else list(np.random.default_rng(T).choice(T, 40, replace=False)) + [T - 1]
