@@ -178,8 +178,10 @@ def test_dispatch_random_assignments(case):
     oracle_pins.check_dispatch_invariants(idx, E, counts, *[t for t in orc.dispatch(G.oracle_dims(wl), idx)[1:]])
 
 
-def test_route_entry_point_matches_forward_routing():
-    wl = inputs.WORKLOADS["decode32"]
+@pytest.mark.parametrize("T", [8, 32])  # the forward call's top-k + dispatch: one work-group / two kernels
+def test_route_entry_point_matches_forward_routing(T):
+    wl = inputs.WORKLOADS["decode32"] if T == 32 else inputs.Workload("flint_T8", T, 2048, 256, 6, 512, 1024,
+                                                                       True, 0)
     w, x = _layer(wl)
     d = api.dims_of(wl)
     idx, tw = api.route(d, x, w["router"], w.get("bias"))
@@ -187,8 +189,10 @@ def test_route_entry_point_matches_forward_routing():
     assert torch.equal(idx, idx2) and torch.equal(tw, tw2)
 
 
-@pytest.mark.parametrize("T", [37, 1500, 4100])  # one wave per token (T <= 4096), 16-lane groups above
-def test_route_exact_ties_go_to_the_lower_index(T):
+# one wave per token (T <= 4096), 16-lane groups above; T = 12 through the
+# forward call, whose top-k shares a work-group with the dispatch (T <= 16)
+@pytest.mark.parametrize("T,via", [(12, "forward"), (37, "route"), (1500, "route"), (4100, "route")])
+def test_route_exact_ties_go_to_the_lower_index(T, via):
     """Router rows in groups of four identical rows, group g scaled by (1 + g):
     the four experts of a group get equal float32 scores on both sides, so with
     K = 6 the boundary falls inside a group for every token and the selection
@@ -200,7 +204,12 @@ def test_route_exact_ties_go_to_the_lower_index(T):
     router = ((1.0 + (torch.arange(E) // 4).float())[:, None] * r0[None, :]).to(torch.bfloat16)
     x = torch.randn(T, H, generator=g).to(torch.bfloat16)
     wl = inputs.custom("ties", T, H, E, K, 64, 0, True)
-    idx, tw = api.route(api.dims_of(wl), x.cuda(), router.cuda(), None)
+    if via == "route":
+        idx, tw = api.route(api.dims_of(wl), x.cuda(), router.cuda(), None)
+    else:
+        w = {k: (v.cuda() if v is not None else None) for k, v in inputs.make_layer(wl, 0, "cpu").items()}
+        w["router"] = router.cuda()
+        _, idx, tw = api.forward(api.dims_of(wl), x.cuda(), w, return_routing=True)
     dd = G.oracle_dims(wl)
     xh, rh = inputs.to_numpy_f32(x), inputs.to_numpy_f32(router)
     o_idx, o_w, _ = orc.route(dd, xh, rh, None)
