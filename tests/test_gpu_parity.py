@@ -44,6 +44,7 @@ SMALL = [
     ("t5_noshr",  5,  64,  8,  3, 64,  0,   True,  False),
     ("t17_e20",   17, 192, 20, 3, 128, 64,  True,  True),
     ("t33",       33, 256, 32, 6, 64,  128, True,  False),
+    ("t24_s4",    24, 256, 16, 2, 64,  256, True,  False),   # shared down split 4 ways
     ("t40_kE",    40, 128, 8,  8, 64,  64,  True,  False),
     ("t64_k1",    64, 128, 16, 1, 128, 64,  True,  True),
     ("t100_f32",  100, 128, 24, 4, 64, 128, False, True),
