@@ -53,7 +53,10 @@ KERNEL_SOURCES = {
     "k_expert_stream_mx4": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream_mx4.hip"],
     "k_tiled": ["common.hpp", "gemm_core.hpp", "launch.hpp", "tiled.hip"],
 }
-STREAM_MAX_T = 512  # largest batch the library serves with the streaming kernels
+# largest bf16 batches the library serves with the streaming kernels (a MoE
+# layer, a dense layer); larger ones go to the tiled kernels
+STREAM_MAX_T = 384
+DENSE_STREAM_MAX_T = 128
 
 
 def parse():
@@ -264,7 +267,7 @@ def bench_dense(args, wl):
     layer_bytes = 3 * I * H * eb + T * H * eb + T * H * 4
     layer_flops = 6 * T * I * H
     big = gu_flops / gu_bytes >= RIDGE  # arithmetic intensity of the gate/up kernel
-    kernel = "k_expert_stream" if T <= STREAM_MAX_T else "k_tiled"
+    kernel = "k_expert_stream" if T <= DENSE_STREAM_MAX_T else "k_tiled"
     digest = sources_digest(kernel)
     kname = f"{kernel}<gate/up> (gate/up GEMM + SwiGLU of the dense layer)"
     traffic = counters_traffic(kernel, wl.name, digest)
@@ -472,7 +475,7 @@ def main():
     layer_flops = float(np.mean([p["flops"]["layer"] for p in per_copy]))
     gu_flops = float(np.mean([p["flops"]["gate_up"] for p in per_copy]))
     big = gu_flops / gate_up_bytes >= RIDGE  # arithmetic intensity of the gate/up kernel
-    kernel = ("k_expert_stream_mx4" if wl.mx4 else "k_expert_stream") if T <= STREAM_MAX_T else "k_tiled"
+    kernel = "k_expert_stream_mx4" if wl.mx4 else ("k_expert_stream" if T <= STREAM_MAX_T else "k_tiled")
     digest = sources_digest(kernel)
     traffic = counters_traffic(kernel, wl.name, digest)
     kname = f"{kernel}<gate/up> (grouped gate/up GEMM + SwiGLU, routed and shared)"

@@ -309,13 +309,16 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 
 ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf16)
 {
-    if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
-        return ExpertTiles{stream_bm1(T, K), 0, stream_bm2(), 0, true, true, false};
-    // Small batches (decode): split-k kernels over 32-row tiles, so that one
-    // tile holds every row an expert gets and each weight is read once.
-    if (T <= 512) return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};
-    if (tiled_eligible(T, K, E, H, I, Is, bf16))
-        return ExpertTiles{tiled_bm1(T, K, E, Is), 0, tiled_bm2(T, K, E), 0, false, false, true};
+    const bool tiled = tiled_eligible(T, K, E, H, I, Is, bf16);
+    const int small_max = tiled ? (K > 0 ? kTiledFromT : kDenseTiledFromT) - 1 : kStreamMaxT;
+    if (T <= small_max) {
+        if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
+            return ExpertTiles{stream_bm1(T, K), 0, stream_bm2(), 0, true, true, false};
+        // Small batches (decode): split-k kernels over 32-row tiles, so that one
+        // tile holds every row an expert gets and each weight is read once.
+        return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};
+    }
+    if (tiled) return ExpertTiles{tiled_bm1(T, K, E, Is), 0, tiled_bm2(T, K, E), 0, false, false, true};
     return ExpertTiles{128, 64, 128, 128, false, false, false};
 }
 

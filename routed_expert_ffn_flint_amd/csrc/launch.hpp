@@ -44,8 +44,21 @@ constexpr int kTopkTile = 256;
 // Maximum supported sizes.
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
-// Largest batch served by the persistent weight-streaming expert kernels.
+// Largest batch the persistent weight-streaming expert kernels (and the
+// split-k small-batch kernels) serve.
 constexpr int kStreamMaxT = 512;
+// Where the LDS-tiled kernels take over when the shape allows them (bf16):
+// from 385 rows for a MoE layer (Flint shape: T = 512 401 -> 385 us; even at
+// 384), from 129 rows for a dense layer, whose weights the streaming kernels
+// read again for every 32 rows (T = 192: 108 -> 74 us; even at 128).
+#ifndef FLINT_TILED_FROM_T
+#define FLINT_TILED_FROM_T 385
+#endif
+#ifndef FLINT_DENSE_TILED_FROM_T
+#define FLINT_DENSE_TILED_FROM_T 129
+#endif
+constexpr int kTiledFromT = FLINT_TILED_FROM_T;
+constexpr int kDenseTiledFromT = FLINT_DENSE_TILED_FROM_T;
 
 // Tile shapes of the expert kernels for one launch regime.
 struct ExpertTiles {

@@ -61,9 +61,6 @@
 #define FLINT_ST_WGS2 2  // down
 #endif
 
-#ifndef FLINT_ST_MAXT
-#define FLINT_ST_MAXT 512  // largest batch served by these kernels
-#endif
 #ifndef FLINT_ST_MB2
 #define FLINT_ST_MB2 2  // down items: MB2 blocks of 16 rows
 #endif
@@ -310,7 +307,7 @@ static int unroll_down(int I, int Is)
 
 bool stream_eligible(int T, int H, int I, int Is)
 {
-    return T <= FLINT_ST_MAXT && unroll_gate_up(H) > 0 && unroll_down(I, Is) > 0;
+    return T <= kStreamMaxT && unroll_gate_up(H) > 0 && unroll_down(I, Is) > 0;
 }
 // (routed layers only: a dense layer's gate/up items are all shared-expert
 // items, and there the 32 x 64 items measured faster at T = 32, 18 vs 22 us)

@@ -470,7 +470,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
 #define FLINT_TL_GU_BIG 3  // gate/up from there: 2 CfgBig, 3 CfgBig8 (or 0, 1)
 #endif
 #ifndef FLINT_TL_DN_SMALL
-#define FLINT_TL_DN_SMALL 0
+#define FLINT_TL_DN_SMALL 6  // (T = 2048: 128 x 256 tiles 154 -> 144 us; even at 4096)
 #endif
 #ifndef FLINT_TL_DN_BIG
 #define FLINT_TL_DN_BIG 3  // (T = 16384: 8 waves measured 3% faster for the layer than 4)

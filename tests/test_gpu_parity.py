@@ -87,10 +87,10 @@ def test_decode32_every_token():
           f"distinct experts={len(np.unique(st['idx']))}")
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 17, 33, 200, 512, 513])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 33, 200, 384, 385, 512])
 def test_flint_layer_small_batches(T):
     """Flint-shaped layer (H=2048, 256 experts top-6, 512/1024 wide) at batch
-    sizes around the decode kernels' range (up to 512 tokens; 513 takes the
+    sizes around the decode kernels' range (up to 384 tokens; 385 takes the
     tiled kernels; up to 16 tokens top-k and dispatch share one work-group):
     routing of every token, outputs of sampled tokens."""
     wl = inputs.Workload(f"flint_T{T}", T, 2048, 256, 6, 512, 1024, True, 5)
@@ -356,6 +356,8 @@ DENSE_CASES = [
     ("d_t1",        1,    128,  192,  True),
     ("d_t33",       33,   256,  320,  True),
     ("d_t7_f32",    7,    128,  64,   False),
+    ("d_t128",      128,  256,  512,  True),    # the largest dense batch on the streaming kernels
+    ("d_t129",      129,  256,  512,  True),    # the smallest on the tiled kernels, down split 8 ways
     ("d_t600",      600,  256,  512,  True),    # large-batch (tiled) kernels, down split 8 ways
     ("d_t1000",     1000, 256,  6144, True),    # 256 x 256 gate/up tiles, ragged last tile
     ("d_t700_f32",  700,  128,  128,  False),   # float32 large-batch kernels
