@@ -93,7 +93,7 @@ struct Cfg {
 #define FLINT_TL_S_ST 5
 #endif
 #ifndef FLINT_TL_N_ST
-#define FLINT_TL_N_ST 4
+#define FLINT_TL_N_ST 3
 #endif
 #ifndef FLINT_TL_B_ST
 #define FLINT_TL_B_ST 4
@@ -102,7 +102,10 @@ using CfgSmall = Cfg<128, 128, 64, 64, FLINT_TL_S_BK, FLINT_TL_S_ST>;  // 4 wave
 using CfgWide = Cfg<256, 128, 128, 64, 32, 6>;                         // 4 waves
 using CfgBig = Cfg<256, 256, 128, 128, 32, FLINT_TL_B_ST>;             // 4 waves
 using CfgBig8 = Cfg<256, 256, 128, 64, 32, FLINT_TL_B_ST>;             // 8 waves
-using CfgWideN = Cfg<128, 256, 64, 64, 32, FLINT_TL_N_ST>;              // 8 waves
+#ifndef FLINT_TL_N_BK
+#define FLINT_TL_N_BK 64  // 128 x 256 tiles: 64-wide slices in 3 stages (T = 4096: 570 -> 560 us vs 32 x 4)
+#endif
+using CfgWideN = Cfg<128, 256, 64, 64, FLINT_TL_N_BK, FLINT_TL_N_ST>;   // 8 waves
 
 // Item of this work-group, or -1 (see the file comment).  Work-groups are
 // dealt to the XCDs round-robin (blockIdx.x % 8 is the XCD); the grid is sized
