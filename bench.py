@@ -24,6 +24,9 @@ Prints ONE JSON line.  Beside the headline throughput:
                 kernel's sources have changed since it was taken;
   step_us_percentiles  p10 / median / p90 of single steps (a third pass,
                 an event pair around each step);
+  device, hbm_read_measured_GBs  the GPU's name, compute units and peak clock
+                as the runtime reports them, and the read rate of row sums
+                over 1 GiB (a practical ceiling beside the 8 TB/s spec);
   cpu_baseline  the oracle (plain fp64 C) timed on the host on a bounded
                 sample of the same workload.
 """
@@ -84,6 +87,35 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n}, "launches": 5}))
+
+
+def device_and_read_rate():
+    """The GPU as the runtime reports it (compute units, peak clock) and a
+    measured HBM read rate: row sums of a 1 GiB float32 tensor (rows of 1024;
+    torch's whole-tensor sum reads at only ~60% of this), best of 6."""
+    import torch
+
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    dev = torch.cuda.current_device()
+    attr = {}
+    for name, code in (("clock_khz", 5), ("cus", 63)):  # hipDeviceAttributeClockRate, ...MultiprocessorCount
+        v = ctypes.c_int()
+        attr[name] = int(v.value) if hip.hipDeviceGetAttribute(ctypes.byref(v), code, dev) == 0 else None
+    props = torch.cuda.get_device_properties(dev)
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    best = float("inf")
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        x.view(-1, 1024).sum(1)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del x
+    return ({"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": attr["cus"],
+             "clock_mhz": None if attr["clock_khz"] is None else attr["clock_khz"] / 1000.0},
+            (1 << 30) / (best * 1e-3) / 1e9)
 
 
 class HipEvents:
@@ -298,6 +330,7 @@ def bench_dense(args, wl):
         "stages_us": stage_us,
         "step_us_percentiles": step_percentiles(step, n_prof),
     }
+    result["device"], result["hbm_read_measured_GBs"] = device_and_read_rate()
     if not args.no_cpu_baseline:
         from oracle import oracle as orc
         o = orc.default()
@@ -513,6 +546,7 @@ def main():
         "stages_us": stage_us,
         "step_us_percentiles": step_percentiles(step, n_prof),
     }
+    result["device"], result["hbm_read_measured_GBs"] = device_and_read_rate()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layers[0], x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
