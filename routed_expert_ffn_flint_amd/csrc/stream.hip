@@ -137,29 +137,13 @@ __global__ __launch_bounds__(256, GATE_UP ? FLINT_ST_WGS1 : FLINT_ST_WGS2) void 
         const S *wa, *wb;  // gate/up (GATE_UP) or the down matrix (wa)
         it.ysplit = 0;
         if (item < n_shared_items) {
-            // shared down items come in shared_splits parts of the reduction.
-            // A unit u = (column tile, part) has its own weights.  Up to 64
-            // tokens its row blocks m sit 8 items apart, in groups of 8 units,
-            // so that they run at the same time on one XCD (work-group w is
-            // on XCD w % 8, item i on work-group i % grid) and read the weights
-            // once from HBM (T = 32: gate/up + down 160.6 -> 158.5 us; at
-            // T = 256, 8 row blocks, the plain order is faster).
+            // shared down items come in shared_splits parts of the reduction
             const int nsplit = GATE_UP ? 1 : (a.shared_splits > 1 ? a.shared_splits : 1);
-            const int nrt = (a.T + BM - 1) / BM, units = ntn_shared * nsplit;
-            int m, u;
-            if (a.T <= FLINT_ST_SMALL_T) {
-                const int g = item / (8 * nrt), r = item % (8 * nrt);
-                const int size = min(8, units - 8 * g);
-                m = r / size;
-                u = 8 * g + r % size;
-            } else {
-                m = item / units;
-                u = item % units;
-            }
-            it.ysplit = u % nsplit;
+            const int sh = item / nsplit;
+            it.ysplit = item % nsplit;
             it.shared = 1;
-            it.row0 = m * BM;
-            nt = u / nsplit;
+            it.row0 = (sh / ntn_shared) * BM;
+            nt = sh % ntn_shared;
             it.row_end = a.T;
             it.kdim = GATE_UP ? H : a.Is;
             klen = it.kdim / nsplit;
