@@ -7,14 +7,21 @@
 // turns the per-expert work into dense row blocks.
 //
 //   k_router_logits  z[t][e] = x[t] . router[e] (+ bias[e])   MFMA, fp32 accumulate
-//   k_topk_dispatch  per tile of 256 tokens: fp32 sigmoid score, top-K by
-//                    wave-wide argmax (equal scores: lower expert index), weights
-//                    s / sum(s) over the K selected, then a per-expert bitmask of
-//                    the tile's tokens gives each pair its rank among earlier
-//                    tokens of the tile and the tile's per-expert histogram.
-//                    When the whole batch is one tile the same work-group also
-//                    scans the counts, scatters the permutation and writes the
-//                    expert kernels' tile lists.
+//                    (batches below 1024 tokens; larger ones use the tiled GEMM)
+//   k_topk_wave      one token per wave (up to 4096 tokens): fp32 sigmoid
+//                    scores, the K-th largest found by a bitwise search with
+//                    wave-wide counts, ties to the lower expert index, weights
+//                    s / sum(s) over the K selected
+//   k_topk<16>       the same selection, 16 lanes per token, by merging sorted
+//                    candidate lists (larger batches)
+//   k_dispatch_tile  per tile of 256 tokens: a per-expert bitmask of the tile's
+//                    tokens gives each pair its rank among earlier tokens of
+//                    the tile and the tile's per-expert histogram.  When the
+//                    whole batch is one tile the same work-group also scans the
+//                    counts, scatters the permutation and writes the expert
+//                    kernels' tile lists.
+//   k_topk_dispatch_small  up to 16 tokens: the top-k of k_topk_wave and the
+//                    one-tile dispatch in a single work-group
 //   k_dispatch_scan  (more than one tile) column scan of the tile histograms,
 //                    expert offsets, tile lists.
 //   k_dispatch_scatter (more than one tile) slot = offset + tile base + rank.

@@ -9,16 +9,17 @@
 // With hundreds of rows per expert the expert products are real GEMMs, so both
 // operands are staged through LDS and reused:
 //   - a work-group computes a BM x BN output tile; its waves each own a
-//     WM x WN block built from 16x16x32 bf16 MFMAs; k runs in slices of 64;
+//     WM x WN block built from 16x16x32 bf16 MFMAs; k runs in slices of BK =
+//     32 or 64 (per configuration);
 //   - operands go from global memory straight into LDS
 //     (global_load_lds_dwordx4: lane l of a wave's load lands at the
 //     instruction's LDS base + 16 l), so no registers hold them in flight and
 //     no LDS write instructions are issued;
-//   - a stage holds the tile's BM A rows then its BN B rows, 128 bytes each
-//     (one 64-element slice).  The 16-byte chunk c of row r is stored at chunk
-//     position c ^ (r & 7): each load instruction covers 8 whole rows (every
-//     row one 128-byte global segment), and a fragment read -- 16 rows, one
-//     chunk -- touches 16 distinct bank groups;
+//   - a stage holds the tile's BM A rows then its BN B rows, 2 BK bytes each.
+//     The 16-byte chunk c of row r is stored at chunk position c ^ (r & 7)
+//     (BK = 64: a load instruction covers 8 whole rows, each one 128-byte
+//     global segment) or c ^ ((r >> 1) & 3) (BK = 32: 16 rows of 64 bytes), so
+//     a fragment read -- 16 rows, one chunk -- touches 16 distinct bank groups;
 //   - slice s is fetched into stage s % STAGES at iteration s - (STAGES - 1),
 //     behind STAGES - 1 iterations of MFMA work.  One barrier per iteration:
 //     after it every wave's share of the current slice has landed (each wave
@@ -38,7 +39,11 @@
 //     go n-tile outer over groups of 8 row tiles, so that both operands repeat
 //     in L2 (dense T = 4096 gate/up: 251 -> 235 us; its L2 misses had been
 //     14x the algorithmic bytes).  The down product deals each XCD an eighth
-//     of the shared and an eighth of the routed items.
+//     of the shared and an eighth of the routed items;
+//   - waves whose rows are all padding (an expert's last tile) only fetch
+//     their share and keep the barriers;
+//   - a dense layer's down product splits its reduction over the width into
+//     partial arrays (the combine adds them) to fill the CUs.
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
