@@ -114,6 +114,19 @@ def _check_dispatch_of(wl, gi):
     return counts
 
 
+@pytest.mark.parametrize("T", [5, 600])
+def test_largest_supported_shape(T):
+    """The largest widths the library takes (H = 8192, I = Is = 4096, K = 8; 32
+    experts to bound the memory): T = 5 on the streaming kernels (every
+    token), T = 600 on the tiled kernels (routing of every token, outputs of
+    sampled ones)."""
+    wl = inputs.Workload(f"max_T{T}", T, 8192, 32, 8, 4096, 4096, True, 9)
+    w, x = _layer(wl)
+    sample = list(range(T)) if T <= 8 else [0, 1, T // 3, T // 2, T - 2, T - 1]
+    st = G.parity_sampled(wl, w, x, sample)
+    print(f"max_T{T}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
+
+
 @pytest.mark.parametrize("name", ["prefill4096", "skew16384"])
 def test_full_size_layer_sampled(name):
     wl = inputs.WORKLOADS[name]
