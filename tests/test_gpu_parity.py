@@ -362,6 +362,15 @@ def test_mx4_largest_batch_every_token():
     print(f"mx4_t512: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
 
 
+def test_mx4_largest_widths():
+    """MXFP4 at the largest widths it takes (H = 8192, I = Is = 4096, K = 8; 32
+    experts to bound the memory), T = 5, every token."""
+    wl = inputs.custom("mx4_max", 5, 8192, 32, 8, 4096, 4096, True, seed=8, mx4=True)
+    w, x = _layer(wl)
+    st = G.parity_mx4(wl, w, x)
+    print(f"mx4_max: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
+
+
 # ---- dense MLP layer (flint_dense_mlp) ---------------------------------------
 
 DENSE_CASES = [
@@ -419,6 +428,18 @@ def test_dense_bf16_output(shape):
     wl = inputs.custom("d_bf16out", T, H, 0, 0, I, 0, True, seed=2, dense=True)
     w, x = _dense(wl)
     _dense_check(wl, w, x, out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("T", [5, 200])
+def test_dense_largest_widths(T):
+    """The dense layer at the largest widths it takes (H = 8192, width 16384):
+    T = 5 on the streaming kernels (every token), T = 200 on the tiled ones
+    (sampled tokens)."""
+    wl = inputs.custom(f"d_max_T{T}", T, 8192, 0, 0, 16384, 0, True, seed=17, dense=True)
+    w, x = _dense(wl)
+    rows = None if T <= 8 else np.array([0, 1, T // 2, T - 1])
+    _, rel = _dense_check(wl, w, x, rows=rows)
+    print(f"d_max_T{T}: rel_err={rel:.3g}")
 
 
 def test_dense4096_sampled():
