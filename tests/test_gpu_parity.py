@@ -46,6 +46,7 @@ SMALL = [
     ("t33",       33, 256, 32, 6, 64,  128, True,  False),
     ("t24_s4",    24, 256, 16, 2, 64,  256, True,  False),   # shared down split 4 ways
     ("t40_kE",    40, 128, 8,  8, 64,  64,  True,  False),
+    ("t24_e256_k8", 24, 2048, 256, 8, 512, 1024, True, True),  # the most experts and the largest K
     ("t64_k1",    64, 128, 16, 1, 128, 64,  True,  True),
     ("t100_f32",  100, 128, 24, 4, 64, 128, False, True),
     ("t300",      300, 256, 64, 6, 128, 128, True, False),   # two dispatch tiles
