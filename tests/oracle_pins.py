@@ -376,11 +376,16 @@ def pin_mx4_element_table(orc):
 
 def pin_mx4_scale(orc):
     # E8M0 byte b means 2^(b-127); 255 is NaN.  Code 2 is 1.0, code 7 is 6.0.
+    # The decoded value is a float32 product: 6 * 2^127 (b = 254) is past the
+    # largest float32 and so decodes to +inf.
+    f32_max = float(np.finfo(np.float32).max)
     for b in (0, 1, 100, 127, 200, 254):
         q, s = _mx4_row([2, 7] * 16, b)
         got = orc.mx4_dequant(q, s)[0]
         assert got[0] == np.float32(math.ldexp(1.0, b - 127)), (b, got[0])
-        assert got[1] == np.float32(6.0 * math.ldexp(1.0, b - 127)), (b, got[1])
+        six = 6.0 * math.ldexp(1.0, b - 127)
+        assert got[1] == (np.float32(six) if six <= f32_max else np.float32(np.inf)), (b, got[1])
+    assert np.isposinf(orc.mx4_dequant(*_mx4_row([7] * 32, 254))[0][0])
     q, s = _mx4_row([2] * 32, 255)
     assert np.all(np.isnan(orc.mx4_dequant(q, s)))
 
