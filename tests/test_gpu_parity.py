@@ -7,6 +7,8 @@ named workloads run at full size: routing of every token is checked, the
 dispatch permutation is checked bit for bit, and the outputs of sampled tokens
 are recomputed by the oracle one by one.  Bars are in gpu_common.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -147,6 +149,37 @@ def test_full_size_layer_sampled(name):
           f"{counts.max() / mean:.1f} min {counts.min()} experts>10x mean {(counts > 10 * mean).sum()}")
     if wl.zipf_bias:
         assert counts.max() > 10 * mean  # the skewed workload really is skewed
+
+
+def test_routed_outputs_past_2_31_elements():
+    """A Flint-shape batch whose routed outputs [T*K, H] span more than 2^31
+    float32 elements (T = 180000: 1.08 M slots of 2048).  The dispatch
+    permutation is checked bit for bit; the routing and outputs of sampled
+    tokens are recomputed by the oracle.  The sample includes tokens whose
+    slots lie past element 2^31, where a 32-bit offset would wrap."""
+    T = 180_000
+    wl = dataclasses.replace(inputs.WORKLOADS["prefill4096"], name="flint_T180000", T=T)
+    K, H = wl.top_k, wl.hidden
+    assert T * K * H > 2**31
+    w, x = _layer(wl)
+    out, idx, tw = G.gpu_layer(wl, w, x)
+    gi, gw = idx.cpu().numpy(), tw.cpu().numpy()
+    _check_dispatch_of(wl, gi)
+    _, _, _, slot_of = orc.dispatch(G.oracle_dims(wl), gi)
+    far = np.nonzero((slot_of.reshape(T, K).astype(np.int64) * H >= 2**31).any(1))[0]
+    assert len(far) > 0
+    rng = np.random.default_rng(2)
+    sample = sorted(set(far[:: max(1, len(far) // 24)][:24].tolist())
+                    | set(rng.choice(T, 16, replace=False).tolist()) | {0, T - 1})
+    rows = torch.as_tensor(sample, device=x.device)
+    xh = inputs.to_numpy_f32(x.index_select(0, rows))
+    d = G.oracle_dims(wl)
+    o_idx, o_w, tie = orc.route(d, xh, inputs.to_numpy_f32(w["router"]), inputs.to_numpy_f32(w.get("bias")))
+    nties = G.check_routing(gi[sample], gw[sample], o_idx, o_w, tie, wl.name)
+    wh = G.host_weights(w, set(gi[sample].ravel().tolist()))
+    ref, _, _, _ = orc.forward(d, xh, wh, force_idx=gi[sample])
+    rel = G.check_output(out.index_select(0, rows).float().cpu().numpy(), ref, wl.name + " (sampled)")
+    print(f"flint_T180000: {len(far)} tokens with slots past 2^31 elements, rel_err={rel:.3g} near_ties={nties}")
 
 
 def test_stack47_layer_by_layer():
