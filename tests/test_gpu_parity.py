@@ -476,6 +476,19 @@ def test_dense_largest_widths(T):
     print(f"d_max_T{T}: rel_err={rel:.3g}")
 
 
+def test_dense_hidden_past_2_31_elements():
+    """A dense batch whose intermediate [T, width] passes 2^31 elements
+    (T = 140000, width 16384): rows from 131072 on sit past element 2^31,
+    where a 32-bit offset would wrap; sampled rows on both sides."""
+    T, H, I = 140_000, 2048, 16384
+    assert T * I > 2**31
+    wl = inputs.custom("d_T140000", T, H, 0, 0, I, 0, True, seed=19, dense=True)
+    w, x = _dense(wl)
+    rows = np.array([0, 1, 70_000, 131_071, 131_072, 131_073, 135_001, T - 2, T - 1])
+    _, rel = _dense_check(wl, w, x, rows=rows)
+    print(f"d_T140000: rel_err={rel:.3g}")
+
+
 def test_dense4096_sampled():
     wl = inputs.WORKLOADS["dense4096"]
     w, x = _dense(wl)
