@@ -525,3 +525,73 @@ def test_mx4_scale_extremes_and_nan_blocks():
     fin = ~nan_ref.any(axis=1)
     assert fin.sum() >= 5
     G.check_output(got[fin], ref[fin], "mx4_scales")
+
+
+GRAPH_CASES = [
+    # workload,       T
+    ("decode32",      8),     # one-launch top-k + dispatch, streaming experts
+    ("decode32",      32),    # the decode batch
+    ("prefill4096",   600),   # three-kernel dispatch, tiled experts
+    ("decode32_mx4",  32),    # MXFP4 expert weights
+    ("dense32",       32),    # dense layer, streaming
+    ("dense4096",     600),   # dense layer, tiled, split down product
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=[f"{c[0]}_T{c[1]}" for c in GRAPH_CASES])
+def test_graph_replays_match_eager(case):
+    """One call captured in a HIP graph and replayed three times.  Before each
+    replay an eager call on other tokens runs with the same workspace, and the
+    outputs are overwritten, so each replay starts from a dirty workspace.
+    Every replay must equal the eager result bit for bit, routing included."""
+    name, T = case
+    wl = dataclasses.replace(inputs.WORKLOADS[name], name=f"{name}_T{T}", T=T)
+    x = inputs.make_tokens(wl, device="cuda")
+    x2 = inputs.make_tokens(wl, device="cuda", stream=1)
+    if wl.dense:
+        w = inputs.make_dense(wl, 0, "cuda")
+        dd = api.dense_dims_of(wl)
+        ws = api.dense_workspace(dd, T)
+        ref = api.dense_mlp(x, w["gate"], w["up"], w["down"], ws=ws)
+        outs = [torch.empty_like(ref)]
+        refs = [ref]
+
+        def call():
+            api.flint_dense_mlp(dd, x, w["gate"], w["up"], w["down"], outs[0], ws)
+
+        def dirty():
+            api.dense_mlp(x2, w["gate"], w["up"], w["down"], ws=ws)
+    else:
+        w = inputs.make_layer(wl, 0, "cuda")
+        d = api.dims_of(wl)
+        ws = api.workspace(d, T)
+        refs = list(api.forward(d, x, w, ws=ws, return_routing=True))
+        outs = [torch.empty_like(r) for r in refs]
+        if wl.mx4:
+            wst = api.weights_mx4_struct(d, w)
+            entry = api.flint_moe_forward_mx4
+        else:
+            wst = api.weights_struct(d, w)
+            entry = api.flint_moe_forward
+
+        def call():
+            entry(d, x, wst, outs[0], outs[1], outs[2], ws)
+
+        def dirty():
+            api.forward(d, x2, w, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    for r in range(3):
+        dirty()
+        for o in outs:
+            o.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs):
+            assert torch.equal(o.view(torch.uint8), ref.view(torch.uint8)), f"{name} T={T}: replay {r} differs"
