@@ -595,3 +595,29 @@ def test_graph_replays_match_eager(case):
         torch.cuda.synchronize()
         for o, ref in zip(outs, refs):
             assert torch.equal(o.view(torch.uint8), ref.view(torch.uint8)), f"{name} T={T}: replay {r} differs"
+
+
+@pytest.mark.parametrize("T", [32, 600])
+def test_concurrent_streams_with_own_workspaces(T):
+    """Calls on two streams at once, each with its own workspace and inputs,
+    launches interleaved: each result equals its eager one bit for bit (the
+    library keeps no device state between calls)."""
+    wl = dataclasses.replace(inputs.WORKLOADS["prefill4096"], name=f"conc_T{T}", T=T)
+    w = inputs.make_layer(wl, 0, "cuda")
+    d = api.dims_of(wl)
+    xs = [inputs.make_tokens(wl, device="cuda", stream=i) for i in range(2)]
+    wss = [api.workspace(d, T) for _ in range(2)]
+    refs = [api.forward(d, xs[i], w, ws=wss[i], return_routing=True) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [[torch.full_like(r, -1) for r in refs[i]] for i in range(2)]
+    wst = api.weights_struct(d, w)
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(2):
+        for i in (0, 1):
+            api.flint_moe_forward(d, xs[i], wst, *outs[i], wss[i], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for o, ref in zip(outs[i], refs[i]):
+            assert torch.equal(o.view(torch.uint8), ref.view(torch.uint8)), f"T={T} stream {i} differs"
