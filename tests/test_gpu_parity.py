@@ -5,7 +5,10 @@ tiles and leave ragged tails (T not a multiple of the 16/32/128-row tiles or the
 256-token dispatch tile; expert counts that are not multiples of 16).  The
 named workloads run at full size: routing of every token is checked, the
 dispatch permutation is checked bit for bit, and the outputs of sampled tokens
-are recomputed by the oracle one by one.  Bars are in gpu_common.
+are recomputed by the oracle one by one.  Batches whose intermediate arrays
+pass 2^31 elements check the 64-bit offsets.  Calls captured in HIP graphs and
+replayed, and calls on two streams at once, must equal eager calls bit for
+bit.  Bars are in gpu_common.
 """
 import dataclasses
 
