@@ -80,6 +80,17 @@ static double round_f32(double a) { return (double)(float)a; }
 
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
+/* Routing weight of a selected expert: its score over the sum of the selected
+ * scores, as float32.  Every selected float32 score is zero only when every
+ * logit lies below about -103.3 (the sigmoid then underflows float32); the
+ * quotient is 0/0 there, and each selected expert gets the equal share 1/K,
+ * which is what equal scores give. */
+static float weight_of(double s, double sum, int K)
+{
+    if (sum > 0.0) return (float)(s / sum);
+    return (float)(1.0 / K);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Router: logits, sigmoid scores, top-K selection, renormalised weights.
  *
@@ -92,7 +103,7 @@ static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
  *   - selection: order experts by (s descending, e ascending) and keep the
  *     first K; equal float32 scores go to the lower expert index;
  *   - weights w_e = float32( s_e / sum_{j in S} s_j ) -- no scaling factor, no
- *     epsilon;
+ *     epsilon; 1/K each when every selected score is zero (weight_of);
  *   - output order of the selected set: ascending expert index;
  *   - near-tie flag: s_(K) - s_(K+1) < 1e-5 in that ordering (false if K == E).
  */
@@ -141,7 +152,7 @@ static void route_one(const oracle_dims *d, const float *x, const float *wr,
         if (taken[e]) sel_out[n++] = e;
     double sum = 0.0;
     for (int k = 0; k < K; ++k) sum += (double)scores[sel_out[k]];
-    for (int k = 0; k < K; ++k) w_out[k] = (float)((double)scores[sel_out[k]] / sum);
+    for (int k = 0; k < K; ++k) w_out[k] = weight_of((double)scores[sel_out[k]], sum, K);
 }
 
 static int check_dims(const oracle_dims *d)
@@ -305,7 +316,7 @@ int oracle_forward(const oracle_dims *d, int T, const float *x, const float *wr,
                     sel[k] = force_idx[(size_t)t * K + k];
                     sum += (double)scores[sel[k]];
                 }
-                for (int k = 0; k < K; ++k) w[k] = (float)((double)scores[sel[k]] / sum);
+                for (int k = 0; k < K; ++k) w[k] = weight_of((double)scores[sel[k]], sum, K);
             }
             for (int n = 0; n < H; ++n) acc[n] = 0.0;
             for (int k = 0; k < K; ++k) {
@@ -392,7 +403,9 @@ void oracle_round_bf16(const double *in, double *out, int64_t n)
 
 /* ------------------------------------------------------------------------ */
 /* Block-scaled 4-bit expert weights.  The pages' low-bit builds store weights
- * in 4 bits (release news, "Availability": 4-bit weights take roughly 23 GB;
+ * in 4 bits ("Recursive launches Flint: open-weight coding model with 39.8
+ * billion parameters for local execution", section "What Flint is, and how it
+ * is built": 4-bit weights take roughly 23 GB;
  * Kalaris analysis: an NVFP4 build on NVIDIA hardware) without defining a
  * format for these kernels, so the format here is a definition: OCP
  * Microscaling MXFP4.
@@ -483,5 +496,16 @@ int oracle_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Sets the number of threads of the loops over tokens (n >= 1; ignored
+ * without OpenMP).  Used to time the oracle on one core and on all of them. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

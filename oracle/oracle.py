@@ -24,7 +24,7 @@ LIBRARY = os.path.join(_HERE, "liboracle.so")
 def compile_source(src: str, out: str) -> str:
     """Compile an oracle source file with gcc (-O2, IEEE double, no fast-math,
     OpenMP over tokens) into a shared library at ``out``."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.tmp{os.getpid()}"  # per process: parallel test workers may build at once
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
            "-std=c11", "-Wall", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
@@ -99,6 +99,8 @@ class Oracle:
         lib.oracle_param_counts.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         self.lib = lib
         self.path = path
 
@@ -236,6 +238,10 @@ class Oracle:
     def threads(self) -> int:
         """Threads the oracle's OpenMP loops use."""
         return int(self.lib.oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads for the oracle's OpenMP loops from now on."""
+        self.lib.oracle_set_threads(int(n))
 
     def param_counts(self, d: Dims):
         """(router, routed total, one expert, shared expert, active expert params per token)."""

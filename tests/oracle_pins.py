@@ -160,6 +160,58 @@ def pin_routing_limits(orc):
     np.testing.assert_array_equal(w[0], np.float32([0.5, 0.5]))
 
 
+def pin_near_tie_threshold(orc):
+    # The near-tie flag marks tokens whose K-th and (K+1)-th float32 scores
+    # differ by less than 1e-5.  With x = [1] the logits are the router weights;
+    # near 0, sigmoid(-d) = 1/2 - d/4 + O(d^3), so logits 0 and -4g put a gap of
+    # g between the two scores (float32 spacing there is 3e-8, far below the
+    # 1e-7 margins used).  K = 2 of 4 experts; the boundary is between the
+    # expert with logit 0 and the one with logit -4g.
+    d = dims(1, 4, 2, 1, 0, False)
+    for gap, flagged in ((0.9e-5, True), (1.1e-5, False), (0.5e-5, True), (2e-5, False)):
+        wr = np.array([[3.0], [0.0], [-4.0 * gap], [-3.0]], np.float32)
+        idx, _, tie = orc.route(d, np.ones((1, 1), np.float32), wr)
+        np.testing.assert_array_equal(idx, [[0, 1]])
+        assert bool(tie[0]) == flagged, (gap, bool(tie[0]))
+    # Only the boundary gap counts: a gap of 4e-6 between the first and second
+    # scores, 1.1e-5 at the boundary -> not flagged.
+    wr = np.array([[1.6e-5], [0.0], [-4.4e-5], [-3.0]], np.float32)
+    _, _, tie = orc.route(d, np.ones((1, 1), np.float32), wr)
+    assert not tie[0]
+    # K = E: no (K+1)-th score, never flagged, even with equal scores.
+    _, _, tie = orc.route(dims(1, 2, 2, 1, 0, False), np.ones((1, 1), np.float32),
+                          np.zeros((2, 1), np.float32))
+    assert not tie[0]
+
+
+def pin_routing_subnormal_scores(orc):
+    # Below z = -87.3 the sigmoid, e^z / (1 + e^z) ~ e^z, is a float32 subnormal
+    # (spacing 2^-149 = 1.4e-45); it stays nonzero down to z ~ -103.3.  Logits
+    # -95 and -95 + ln 2 give scores 5.5e-42 and twice that (about 3900 and
+    # 7800 subnormal steps), so the weights are 1/3 and 2/3 to within 1e-3
+    # (the softmax limit of the sigmoid weights); logit -110 underflows to 0.
+    d = dims(1, 3, 2, 1, 0, False)
+    wr = np.array([[-95.0], [-95.0 + math.log(2.0)], [-110.0]], np.float32)
+    idx, w, _ = orc.route(d, np.ones((1, 1), np.float32), wr)
+    np.testing.assert_array_equal(idx, [[0, 1]])
+    np.testing.assert_allclose(w[0], [1 / 3, 2 / 3], atol=1e-3)
+    s = orc.scores(d, np.ones((1, 1), np.float32), wr)[0]
+    assert 0.0 < s[0] < np.finfo(np.float32).tiny and s[2] == 0.0
+    np.testing.assert_allclose(s[1] / s[0], 2.0, rtol=1e-3)
+
+
+def pin_routing_zero_scores(orc):
+    # Every logit below -103.3: every float32 score is 0, so all are equal: the
+    # lowest K ids are selected and, the normalisation being 0/0, each gets 1/K.
+    d = dims(1, 5, 3, 1, 0, False)
+    wr = np.array([[-120.0], [-104.5], [-300.0], [-150.0], [-110.0]], np.float32)
+    idx, w, tie = orc.route(d, np.ones((1, 1), np.float32), wr)
+    np.testing.assert_array_equal(idx, [[0, 1, 2]])
+    np.testing.assert_array_equal(w, np.full((1, 3), np.float32(1 / 3)))
+    assert tie[0]
+    np.testing.assert_array_equal(orc.scores(d, np.ones((1, 1), np.float32), wr), np.zeros((1, 5), np.float32))
+
+
 def pin_routing_bias(orc):
     # The bias enters the logit: a large bias on expert 2 makes it selected.
     d = dims(1, 4, 1, 1, 0, False)
@@ -495,7 +547,8 @@ def pin_dense_is_the_shared_expert_alone(orc):
 
 
 ALL_PINS = [pin_param_counts, pin_bf16_rounding, pin_routing_hand_top2, pin_routing_hand_all,
-            pin_routing_equal_logits, pin_routing_tie_break, pin_routing_limits, pin_routing_bias,
+            pin_routing_equal_logits, pin_routing_tie_break, pin_near_tie_threshold,
+            pin_routing_subnormal_scores, pin_routing_zero_scores, pin_routing_limits, pin_routing_bias,
             pin_routing_library, pin_expert_closed_form, pin_bf16_intermediate, pin_dense_mixture,
             pin_shared_split, pin_token_permutation, pin_dispatch_hand, pin_dispatch_invariants,
             pin_rmsnorm, pin_mx4_element_table, pin_mx4_scale, pin_mx4_layout, pin_mx4_tiled_layout,

@@ -48,8 +48,14 @@ MUTANTS = [
      "for (int n = 0; n < H; ++n) acc[n] += 0.0 * y[n];"),
     ("transposed_down", "acc += (double)wd[(size_t)n * width + i] * h_scratch[i];",
      "acc += (double)wd[(size_t)i * H + n] * h_scratch[i];"),
-    ("no_normalisation", "w_out[k] = (float)((double)scores[sel_out[k]] / sum);",
-     "w_out[k] = (float)((double)scores[sel_out[k]]);"),
+    ("no_normalisation", "if (sum > 0.0) return (float)(s / sum);", "if (sum > 0.0) return (float)s;"),
+    ("zero_sum_gives_nan", "return (float)(1.0 / K);", "return (float)(s / sum);"),
+    ("near_tie_threshold_1e-2", "tie = gap < 1e-5;", "tie = gap < 1e-2;"),
+    ("near_tie_threshold_1e-6", "tie = gap < 1e-5;", "tie = gap < 1e-6;"),
+    ("near_tie_gap_at_the_top", "double gap = (double)scores[picked[K - 1]] - (double)scores[next];",
+     "double gap = (double)scores[picked[0]] - (double)scores[picked[K > 1 ? 1 : 0]];"),
+    ("sigmoid_in_float32", "static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }",
+     "static double sigmoid(double z) { return 1.0f / (1.0f + expf((float)-z)); }"),
     ("no_h_rounding", "h_scratch[i] = d->h_is_bf16 ? round_bf16(a) : round_f32(a);", "h_scratch[i] = a;"),
     ("bf16_truncation", "double q = rint(ldexp(a, -ulp_exp));", "double q = trunc(ldexp(a, -ulp_exp));"),
     ("bias_ignored_in_route", "        if (bias) acc += (double)bias[e];\n        float z = (float)acc;\n        scores[e]",
