@@ -27,8 +27,12 @@ Prints ONE JSON line.  Beside the headline throughput:
   device, hbm_read_measured_GBs  the GPU's name, compute units and peak clock
                 as the runtime reports them, and the read rate of row sums
                 over 1 GiB (a practical ceiling beside the 8 TB/s spec);
+  parity        one layer call (weight copy 0) against the oracle, outside
+                the timed region: near-tie tokens, tokens whose expert set
+                differs, max |gpu - oracle| / rms of the outputs;
   cpu_baseline  the oracle (plain fp64 C) timed on the host on a bounded
-                sample of the same workload.
+                sample of the same workload, on all its threads and on one
+                core, with the host's CPU model.
 """
 from __future__ import annotations
 
@@ -213,32 +217,120 @@ def algorithmic(wl, idx_np):
             "router_bytes": router_bytes, "layer_bytes": layer_bytes, "flops": flops}
 
 
+def host_cpu():
+    """The host's CPU model (as /proc/cpuinfo names it) and its logical CPUs."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "nproc": os.cpu_count(), "usable": len(os.sched_getaffinity(0))}
+
+
+def time_calls(fn, n_tok, target_s):
+    """Calls fn until about target_s seconds have passed (at most 1000 calls):
+    (tokens/s, calls, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            return reps * n_tok / el, reps, el
+
+
+def oracle_baseline(o, run, n_all_tok, n_one_tok, target_s, what):
+    """The oracle timed on all the threads its OpenMP loops use (over tokens)
+    and on one core: run(n) does one call on the first n tokens."""
+    threads = o.threads()
+    v_all, r_all, e_all = time_calls(lambda: run(n_all_tok), n_all_tok, target_s)
+    o.set_threads(1)
+    try:
+        v_one, r_one, e_one = time_calls(lambda: run(n_one_tok), n_one_tok, target_s)
+    finally:
+        o.set_threads(threads)
+    return {"value": v_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, the first {n_all_tok} tokens per call, fp64, {r_all} calls over {e_all:.1f} s "
+                      f"on {threads} threads",
+            "single_core": {"value": v_one, "unit": "tokens/s", "cores": 1,
+                            "sample": f"the first {n_one_tok} tokens per call, {r_one} calls over {e_one:.1f} s"},
+            "cpu": host_cpu()}
+
+
+def host_layer_weights(o, wl, w_dev, experts=None):
+    """Exact float32 host copies of a layer's weights for the oracle (MXFP4
+    matrices decoded by the oracle itself); with ``experts``, only those
+    routed experts' matrices (the rest zero)."""
+    from routed_expert_ffn_flint_amd import inputs
+    import torch
+
+    def pick(k, v):
+        if experts is None or k.split("_")[0] not in ("gate", "up", "down"):
+            return v
+        keep = torch.as_tensor(sorted(experts), device=v.device, dtype=torch.long)
+        out = torch.zeros_like(v)
+        out.index_copy_(0, keep, v.index_select(0, keep))
+        return out
+
+    if wl.mx4:
+        return o.mx4_weights({k: (pick(k, v).cpu().numpy() if k.endswith(("_q", "_s")) else inputs.to_numpy_f32(v))
+                              for k, v in w_dev.items()})
+    return {k: inputs.to_numpy_f32(pick(k, v) if v is not None else None) for k, v in w_dev.items()}
+
+
 def cpu_baseline(wl, w_dev, x_dev, target_s):
-    """The oracle on the host: whole-layer forward of the workload's first
-    tokens, repeated until about target_s seconds of work."""
+    """The oracle on the host: whole-layer forward (routing included) of the
+    workload's first tokens, on all threads and on one core."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from oracle import oracle as orc
     from routed_expert_ffn_flint_amd import inputs
 
     o = orc.default()
     d = orc.dims(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, wl.bf16)
-    if wl.mx4:  # the oracle decodes the stored 4-bit weights itself
-        wh = o.mx4_weights({k: (v.cpu().numpy() if k.endswith(("_q", "_s")) else inputs.to_numpy_f32(v))
-                            for k, v in w_dev.items()})
-    else:
-        wh = {k: inputs.to_numpy_f32(v) for k, v in w_dev.items()}
+    wh = host_layer_weights(o, wl, w_dev)
     n_tok = min(wl.T, 32)
     xh = inputs.to_numpy_f32(x_dev[:n_tok])
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        o.forward(d, xh, wh)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or reps >= 1000:
-            break
-    return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": o.threads(), "kind": "oracle",
-            "sample": f"{wl.name} layer (weight copy 0), the first {n_tok} tokens, whole-layer forward "
-                      f"in fp64, repeated {reps}x over {el:.1f} s"}
+    return oracle_baseline(o, lambda n: o.forward(d, xh[:n], wh), n_tok, min(n_tok, 4), target_s / 2,
+                           f"{wl.name} layer (weight copy 0)")
+
+
+def parity_report(wl, w_dev, x_dev, out, idx, tw, max_tokens=512):
+    """The GPU result of one layer call against the oracle, outside the timed
+    region: routing of the checked tokens (near-tie tokens flagged by the
+    oracle, tokens whose expert set differs) and max |gpu - oracle| / rms of
+    their outputs, the oracle run with the GPU's expert sets (tokens spread
+    evenly over the batch when it has more than max_tokens)."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import oracle as orc
+    from routed_expert_ffn_flint_amd import inputs
+    import torch
+
+    o = orc.default()
+    d = orc.dims(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, wl.bf16)
+    T = x_dev.shape[0]
+    rows = np.arange(T) if T <= max_tokens else np.unique(np.linspace(0, T - 1, max_tokens).astype(np.int64))
+    sel = torch.as_tensor(rows, device=x_dev.device)
+    xh = inputs.to_numpy_f32(x_dev.index_select(0, sel))
+    gi = idx.index_select(0, sel).cpu().numpy()
+    gw = tw.index_select(0, sel).cpu().numpy()
+    router = inputs.to_numpy_f32(w_dev["router"])
+    bias = inputs.to_numpy_f32(w_dev.get("bias"))
+    o_idx, o_w, tie = o.route(d, xh, router, bias)
+    differ = np.any(gi != o_idx, axis=1)
+    wh = host_layer_weights(o, wl, w_dev, set(gi.ravel().tolist()))
+    ref, _, rw, _ = o.forward(d, xh, wh, force_idx=gi)
+    g = out.index_select(0, sel).float().cpu().numpy().astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    return {"tokens_checked": int(len(rows)), "near_tie_tokens": int(tie.sum()),
+            "sets_differing": int(differ.sum()),
+            "max_abs_err_over_rms": float(np.max(np.abs(g - ref)) / rms) if rms > 0 else 0.0,
+            "max_weight_err": float(np.max(np.abs(gw - rw))) if gw.size else 0.0,
+            "bar": "sets equal except near ties (K-th/(K+1)-th oracle score gap < 1e-5); "
+                   "max |delta| <= 1e-2 * rms"}
 
 
 def bench_dense(args, wl):
@@ -331,23 +423,24 @@ def bench_dense(args, wl):
         "step_us_percentiles": step_percentiles(step, n_prof),
     }
     result["device"], result["hbm_read_measured_GBs"] = device_and_read_rate()
+    from oracle import oracle as orc
+    o = orc.default()
+    w0 = {k: inputs.to_numpy_f32(v) for k, v in layers[0].items()}
+    # parity of one call on weight copy 0, outside the timed region
+    step(0)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 512 else np.unique(np.linspace(0, T - 1, 512).astype(np.int64))
+    ref = o.dense_mlp(inputs.to_numpy_f32(x)[rows], w0["gate"], w0["up"], w0["down"], h_bf16=wl.bf16)
+    g = out.cpu().numpy()[rows].astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    result["parity"] = {"tokens_checked": int(len(rows)), "max_abs_err_over_rms": float(np.max(np.abs(g - ref)) / rms),
+                        "bar": "max |delta| <= 1e-2 * rms"}
     if not args.no_cpu_baseline:
-        from oracle import oracle as orc
-        o = orc.default()
-        w0 = {k: inputs.to_numpy_f32(v) for k, v in layers[0].items()}
         n_tok = min(T, 32)
         xh = inputs.to_numpy_f32(x[:n_tok])
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            o.dense_mlp(xh, w0["gate"], w0["up"], w0["down"], h_bf16=wl.bf16)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or reps >= 1000:
-                break
-        result["cpu_baseline"] = {"value": reps * n_tok / el, "unit": "tokens/s", "cores": o.threads(),
-                                  "kind": "oracle",
-                                  "sample": f"{wl.name} layer (weight copy 0), the first {n_tok} tokens, fp64, "
-                                            f"repeated {reps}x over {el:.1f} s"}
+        result["cpu_baseline"] = oracle_baseline(
+            o, lambda n: o.dense_mlp(xh[:n], w0["gate"], w0["up"], w0["down"], h_bf16=wl.bf16), n_tok,
+            min(n_tok, 4), args.cpu_seconds / 2, f"{wl.name} layer (weight copy 0)")
     print(json.dumps(result), flush=True)
 
 
@@ -547,6 +640,10 @@ def main():
         "step_us_percentiles": step_percentiles(step, n_prof),
     }
     result["device"], result["hbm_read_measured_GBs"] = device_and_read_rate()
+    # parity of one call (weight copy 0 / the stack's first layer), outside the timed region
+    layer_call(0, xp)
+    torch.cuda.synchronize()
+    result["parity"] = parity_report(wl, layers[0], x, out, idx, tw)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layers[0], x, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -14,10 +14,13 @@
  *
  * For each token x (length H):
  *   z_e   = x . router[e] (+ router_bias[e])            e = 0..E-1, float32
- *   s_e   = sigmoid(z_e)                                 float32
+ *   s_e   = sigmoid(z_e)                                 float32 (a subnormal for
+ *           logits between about -103.3 and -87.3, 0 below, 1 above about 17)
  *   S     = the K experts with the largest s_e (equal scores: lower index first),
  *           reported in ascending expert order
  *   w_e   = s_e / sum_{j in S} s_j                       float32, e in S
+ *           (1/K each when every selected s_e is 0: the quotient is 0/0 there,
+ *           and 1/K is what equal scores give)
  *   h_e   = silu(gate[e] x) * (up[e] x),  silu(g) = g * sigmoid(g), stored in the
  *           layer's dtype
  *   out   = sum_{e in S} w_e * down[e] h_e  +  shared_down (silu(shared_gate x) * (shared_up x))
@@ -161,8 +164,10 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *dims, int32_t T, c
                                         void *const *events);
 
 /* ---- Expert weights in MXFP4 (block-scaled 4-bit) --------------------------
- * The pages' low-bit builds store weights in 4 bits (release news,
- * "Availability": 4-bit weights take roughly 23 GB) without a format for these
+ * The pages' low-bit builds store weights in 4 bits ("Recursive launches
+ * Flint: open-weight coding model with 39.8 billion parameters for local
+ * execution", section "What Flint is, and how it is built": 4-bit weights take
+ * roughly 23 GB) without a format for these
  * kernels; this library defines one: OCP Microscaling MXFP4 values in a tiled
  * byte order.  The values: FP4 E2M1 elements (sign, 2 exponent bits with bias
  * 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E8M0 scale

@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -34,8 +35,7 @@ def build(verbose: bool = False) -> str:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function", f"-I{os.path.join(HERE, '..', 'include')}",
     ]
-    objs = []
-    for src in SOURCES:
+    def compile_one(src):
         obj = os.path.join(out_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [hipcc()] + common + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -48,7 +48,12 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{err}")
         if err.strip() and verbose:
             print(err, file=sys.stderr)
-        objs.append(obj)
+        return obj
+
+    # the sources compile independently: in parallel, a few at a time
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

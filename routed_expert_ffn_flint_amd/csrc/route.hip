@@ -232,9 +232,25 @@ __device__ int finish_offsets_and_lists(int c, int E, int32_t *offsets, int32_t 
     return off;  // expert threadIdx.x's first slot
 }
 
+// sigmoid(z) in float32.  For z < 0 it is e^z / (1 + e^z): 1 / (1 + e^-z)
+// would overflow e^-z to infinity below z = -88.7 and return 0, where the
+// score is still a float32 subnormal (it reaches 0 only below about -103.3).
 __device__ __forceinline__ float score_from_logit(float z)
 {
+    if (z < 0.0f) {
+        const float e = expf(z);
+        return e / (1.0f + e);
+    }
     return 1.0f / (1.0f + expf(-z));
+}
+
+// Routing weight of a selected expert: score / sum of the selected scores,
+// the sum in double.  When every selected score is zero (every logit below
+// about -103.3) the quotient is 0/0; each expert then gets 1/K, the share
+// equal scores get.
+__device__ __forceinline__ float routing_weight(float s, double sum, int K)
+{
+    return sum > 0.0 ? (float)((double)s / sum) : (float)(1.0 / K);
 }
 
 // Selection key of a candidate: larger key = selected first.  Scores are
@@ -428,7 +444,7 @@ __device__ __forceinline__ void write_topk(const uint64_t (&l)[kMaxTopK], int t,
     for (int k = 0; k < kMaxTopK; ++k)
         if (k < K && gl == k) {
             topk_idx[(size_t)t * K + k] = se[k];
-            topk_w[(size_t)t * K + k] = (float)((double)ss[k] / sum);
+            topk_w[(size_t)t * K + k] = routing_weight(ss[k], sum, K);
         }
 }
 
@@ -503,7 +519,7 @@ __device__ __forceinline__ void wave_topk(const float *zt, size_t split_stride, 
     for (int k = 0; k < K; ++k) sum += (double)ls[k];
     if (lane < K) {
         topk_idx[(size_t)t * K + lane] = le[lane];
-        topk_w[(size_t)t * K + lane] = (float)((double)ls[lane] / sum);
+        topk_w[(size_t)t * K + lane] = routing_weight(ls[lane], sum, K);
         if (sel_lds) sel_lds[t * K + lane] = (int16_t)le[lane];  // (a one-tile batch: t is tile-relative)
     }
 }

@@ -5,7 +5,9 @@
 // page, "What runs on each token"): K selected experts of width I per token plus
 // an always-on shared expert of width Is, each a gated three-matrix SwiGLU.
 // Weight format (a definition; the pages' low-bit builds store 4-bit weights,
-// release news, "Availability"): OCP Microscaling MXFP4 -- FP4 E2M1 elements,
+// "Recursive launches Flint: open-weight coding model with 39.8 billion
+// parameters for local execution", section "What Flint is, and how it is
+// built"): OCP Microscaling MXFP4 -- FP4 E2M1 elements,
 // 32-element blocks along the reduction dimension, an E8M0 scale 2^(s-127) per
 // block, two elements per byte with the lower-indexed one in the low nibble --
 // stored in tiles of 16 rows x one block: a tile's codes are its 16 rows' 16

@@ -21,6 +21,7 @@ from routed_expert_ffn_flint_amd import api, inputs
 
 OUT_TOL = 1e-2       # max |delta| / rms(oracle)
 WEIGHT_TOL = 2e-6
+TIE_GAP = 1e-5       # the near-tie threshold on the oracle's K-th / (K+1)-th scores
 
 
 def require_gpu():
@@ -85,17 +86,28 @@ def parity_mx4(wl, w_dev, x_dev, out_dtype=torch.float32):
     bias = inputs.to_numpy_f32(w_dev.get("bias"))
     o_idx, o_w, tie = orc.route(d, xh, router, bias)
     gi, gw = idx.cpu().numpy(), tw.cpu().numpy()
-    nties = check_routing(gi, gw, o_idx, o_w, tie, wl.name)
+    nties = check_routing(gi, gw, o_idx, o_w, tie, wl.name, scores_fn(d, xh, router, bias))
     wh = host_weights_mx4(w_dev, set(gi.ravel().tolist()))
     ref, _, _, _ = orc.forward(d, xh, wh, force_idx=gi)
     rel = check_output(out.float().cpu().numpy(), ref, wl.name)
     return {"near_ties": nties, "rel_err": rel, "idx": gi, "out": out}
 
 
-def check_routing(gpu_idx, gpu_w, ora_idx, ora_w, near_tie, where=""):
-    """Returns the number of near-tie tokens whose sets differ."""
+def check_routing(gpu_idx, gpu_w, ora_idx, ora_w, near_tie, where="", scores_of=None):
+    """Returns the number of near-tie tokens whose sets differ.
+
+    Tokens whose GPU set equals the oracle's: weights within WEIGHT_TOL.  A
+    token whose set differs must be a near tie (oracle K-th and (K+1)-th scores
+    closer than TIE_GAP), and the GPU's set must itself be a correct answer,
+    judged on the oracle's float32 scores (``scores_of(rows)`` returns them,
+    [len(rows), E]): every selected score at least every unselected one minus
+    TIE_GAP; the experts in one set and not the other all within TIE_GAP of the
+    oracle's K-th score; and the GPU's weights equal to the scores renormalised
+    over the GPU's own set (1/K each if they sum to 0)."""
     gpu_idx = np.asarray(gpu_idx)
     ora_idx = np.asarray(ora_idx)
+    gpu_w = np.asarray(gpu_w)
+    K = gpu_idx.shape[1]
     differ = np.any(gpu_idx != ora_idx, axis=1)
     bad = differ & ~np.asarray(near_tie)
     assert not bad.any(), (f"{where}: {int(bad.sum())} tokens route differently without a near tie, "
@@ -104,10 +116,39 @@ def check_routing(gpu_idx, gpu_w, ora_idx, ora_w, near_tie, where=""):
     assert np.all(np.diff(gpu_idx, axis=1) > 0), f"{where}: rows not strictly ascending"
     same = ~differ
     if same.any():
-        dw = np.abs(np.asarray(gpu_w)[same] - np.asarray(ora_w)[same])
+        dw = np.abs(gpu_w[same] - np.asarray(ora_w)[same])
         assert dw.max() <= WEIGHT_TOL, f"{where}: routing weight off by {dw.max():.3g}"
     np.testing.assert_allclose(np.asarray(gpu_w, np.float64).sum(1), 1.0, atol=2e-6)
+    rows = np.nonzero(differ)[0]
+    if len(rows):
+        assert scores_of is not None, f"{where}: tokens differ; their oracle scores are needed to judge them"
+        sc = np.asarray(scores_of(rows), np.float64)
+        E = sc.shape[1]
+        for j, t in enumerate(rows):
+            s = sc[j]
+            sel = gpu_idx[t]
+            assert sel.min() >= 0 and sel.max() < E, f"{where}: token {t}: expert id out of range"
+            mask = np.zeros(E, bool)
+            mask[sel] = True
+            s_k = np.sort(s)[::-1][K - 1]
+            if K < E:
+                assert s[mask].min() >= s[~mask].max() - TIE_GAP, (
+                    f"{where}: token {t}: GPU set {sel.tolist()} is not a top-{K} set "
+                    f"(selected min {s[mask].min():.9g} < unselected max {s[~mask].max():.9g} - {TIE_GAP})")
+            swapped = np.setxor1d(sel, ora_idx[t])
+            assert np.all(np.abs(s[swapped] - s_k) < TIE_GAP), (
+                f"{where}: token {t}: experts {swapped.tolist()} differ from the oracle's set but are not "
+                f"within {TIE_GAP} of the K-th score")
+            tot = s[sel].sum()
+            ref_w = s[sel] / tot if tot > 0 else np.full(K, 1.0 / K)
+            dw = np.max(np.abs(gpu_w[t] - ref_w))
+            assert dw <= WEIGHT_TOL, f"{where}: token {t}: weights off by {dw:.3g} on the GPU's own set"
     return int(differ.sum())
+
+
+def scores_fn(d, xh, router, bias):
+    """scores_of(rows) for check_routing: the oracle's float32 scores of those tokens."""
+    return lambda rows: orc.scores(d, np.asarray(xh)[np.asarray(rows)], router, bias)
 
 
 def check_output(gpu_out, ora_out, where=""):
@@ -135,7 +176,7 @@ def parity_full(wl, w_dev, x_dev, out_dtype=torch.float32):
     xh = inputs.to_numpy_f32(x_dev)
     o_idx, o_w, tie = orc.route(d, xh, wh["router"], wh["bias"])
     gi, gw = idx.cpu().numpy(), tw.cpu().numpy()
-    nties = check_routing(gi, gw, o_idx, o_w, tie, wl.name)
+    nties = check_routing(gi, gw, o_idx, o_w, tie, wl.name, scores_fn(d, xh, wh["router"], wh["bias"]))
     ref, _, _, _ = orc.forward(d, xh, wh, force_idx=gi)
     if out_dtype == torch.bfloat16:
         # compare against the oracle rounded the same way, with one bf16 ulp of slack
@@ -159,7 +200,7 @@ def parity_sampled(wl, w_dev, x_dev, sample, out_dtype=torch.float32):
     bias = inputs.to_numpy_f32(w_dev.get("bias"))
     o_idx, o_w, tie = orc.route(d, xh, router, bias)
     gi, gw = idx.cpu().numpy(), tw.cpu().numpy()
-    nties = check_routing(gi, gw, o_idx, o_w, tie, wl.name)
+    nties = check_routing(gi, gw, o_idx, o_w, tie, wl.name, scores_fn(d, xh, router, bias))
     sample = np.asarray(sorted(set(int(t) for t in sample)))
     experts = set(gi[sample].ravel().tolist())
     wh = host_weights(w_dev, experts)

@@ -4,11 +4,13 @@ Small cases run the oracle on every token, with shapes chosen to span several
 tiles and leave ragged tails (T not a multiple of the 16/32/128-row tiles or the
 256-token dispatch tile; expert counts that are not multiples of 16).  The
 named workloads run at full size: routing of every token is checked, the
-dispatch permutation is checked bit for bit, and the outputs of sampled tokens
-are recomputed by the oracle one by one.  Batches whose intermediate arrays
+dispatch permutation is checked bit for bit, and the outputs of every token
+(prefill4096, skew16384, seven whole layers of stack47) or of sampled tokens
+(the rest) are recomputed by the oracle.  Batches whose intermediate arrays
 pass 2^31 elements check the 64-bit offsets.  Calls captured in HIP graphs and
 replayed, and calls on two streams at once, must equal eager calls bit for
-bit.  Bars are in gpu_common.
+bit.  Router logits pushed far outside their usual range check the sigmoid's
+saturated, subnormal and underflowing scores.  Bars are in gpu_common.
 """
 import dataclasses
 
@@ -59,6 +61,10 @@ SMALL = [
     ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
     ("t2100_big", 2100, 256, 16, 4, 128, 128, True, True),   # 256-row tiles, router split over H
     ("t5000_ns",  5000, 128, 8,  2, 128, 0,   True, False),  # 256-row tiles, no shared expert
+    # float32 layers on the weight-streaming kernels (H, I, Is multiples of 256)
+    ("t40_f32_st",  40,  256, 16, 2, 256, 512, False, False),
+    ("t200_f32_st", 200, 512, 32, 6, 256, 256, False, True),
+    ("t512_f32_st", 512, 256, 16, 4, 256, 256, False, False),  # the largest float32 streaming batch
 ]
 
 
@@ -134,21 +140,16 @@ def test_largest_supported_shape(T):
 
 
 @pytest.mark.parametrize("name", ["prefill4096", "skew16384"])
-def test_full_size_layer_sampled(name):
+def test_full_size_layer_every_token(name):
+    """The prefill and skewed workloads at full size: routing, dispatch and the
+    output of every token against the oracle (every row tile and n-tile of the
+    tiled kernels, the hot experts' many row tiles included)."""
     wl = inputs.WORKLOADS[name]
     w, x = _layer(wl)
-    T = wl.T
-    rng = np.random.default_rng(1)
-    sample = list(rng.choice(T, 48, replace=False)) + [0, T - 1]
-    # include tokens of the most loaded expert (several row tiles of it)
-    st = G.parity_sampled(wl, w, x, sample)
+    st = G.parity_full(wl, w, x)
     counts = _check_dispatch_of(wl, st["idx"])
-    hot = int(np.argmax(counts))
-    hot_tokens = np.nonzero((st["idx"] == hot).any(1))[0]
-    extra = list(hot_tokens[:: max(1, len(hot_tokens) // 16)][:16])
-    G.parity_sampled(wl, w, x, extra)
     mean = counts.mean()
-    print(f"{name}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']} max/mean load "
+    print(f"{name}: every token, rel_err={st['rel_err']:.3g} near_ties={st['near_ties']} max/mean load "
           f"{counts.max() / mean:.1f} min {counts.min()} experts>10x mean {(counts > 10 * mean).sum()}")
     if wl.zipf_bias:
         assert counts.max() > 10 * mean  # the skewed workload really is skewed
@@ -178,18 +179,22 @@ def test_routed_outputs_past_2_31_elements():
     xh = inputs.to_numpy_f32(x.index_select(0, rows))
     d = G.oracle_dims(wl)
     o_idx, o_w, tie = orc.route(d, xh, inputs.to_numpy_f32(w["router"]), inputs.to_numpy_f32(w.get("bias")))
-    nties = G.check_routing(gi[sample], gw[sample], o_idx, o_w, tie, wl.name)
+    nties = G.check_routing(gi[sample], gw[sample], o_idx, o_w, tie, wl.name,
+                            G.scores_fn(d, xh, inputs.to_numpy_f32(w["router"]), inputs.to_numpy_f32(w.get("bias"))))
     wh = G.host_weights(w, set(gi[sample].ravel().tolist()))
     ref, _, _, _ = orc.forward(d, xh, wh, force_idx=gi[sample])
     rel = G.check_output(out.index_select(0, rows).float().cpu().numpy(), ref, wl.name + " (sampled)")
     print(f"flint_T180000: {len(far)} tokens with slots past 2^31 elements, rel_err={rel:.3g} near_ties={nties}")
 
 
+STACK_FULL_LAYERS = (0, 8, 16, 24, 32, 40, 46)
+
+
 def test_stack47_layer_by_layer():
     """47 distinct layers resident in HBM, RMSNorm between layers.  Each layer is
     checked against the oracle fed the GPU's own input to that layer (a flipped
-    near tie would otherwise cascade), on sampled tokens; each RMSNorm is checked
-    on every token."""
+    near tie would otherwise cascade): every token of layers 0, 8, ..., 40 and
+    46, sampled tokens of the others; each RMSNorm is checked on every token."""
     wl = inputs.WORKLOADS["stack47"]
     d = api.dims_of(wl)
     layers = [inputs.make_layer(wl, l, "cuda") for l in range(wl.layers)]
@@ -200,10 +205,15 @@ def test_stack47_layer_by_layer():
     worst = 0.0
     ties = 0
     for l, w in enumerate(layers):
-        sample = rng.choice(wl.T, 6, replace=False)
+        sample = rng.choice(wl.T, 8, replace=False)
         one = inputs.Workload(f"stack47/L{l}", wl.T, wl.hidden, wl.n_experts, wl.top_k, wl.inter,
                               wl.shared_inter, True, wl.seed)
-        st = G.parity_sampled(one, w, x, sample)
+        if l in STACK_FULL_LAYERS:
+            st = G.parity_full(one, w, x)
+            out, _, _ = G.gpu_layer(one, w, x)  # (deterministic: the same bits parity_full checked)
+            st["out"] = out
+        else:
+            st = G.parity_sampled(one, w, x, sample)
         worst = max(worst, st["rel_err"])
         ties += st["near_ties"]
         if l % 8 == 0:
@@ -277,6 +287,80 @@ def test_route_exact_ties_go_to_the_lower_index(T, via):
         np.testing.assert_allclose(tw[t].cpu().numpy(), o_w[t], rtol=0, atol=G.WEIGHT_TOL)
     print(f"ties T={T}: {checked} tokens checked, {boundary_ties} with a tie at the boundary")
     assert checked >= T // 2 and boundary_ties == checked
+
+
+def _extreme_router(regime, E, H):
+    """bf16 router rows c_e * (1, ..., 1) whose products with the tokens below
+    give logits H * s_t * c_e exactly in float32 on both sides:
+    saturated  z in [20, 120]: every score rounds to 1.0 (all equal)
+    subnormal  z in about [-95.2, -88.6]: scores are float32 subnormals, in
+               groups of equal c_e (logit steps of 0.5 between groups)
+    zero       z <= -110: every score underflows to 0"""
+    e = torch.arange(E, dtype=torch.float64)
+    if regime == "saturated":
+        hc = 20.0 + 40.0 * e / E
+    elif regime == "subnormal":
+        hc = -(88.6 + 4.4 * ((e * 37) % E) / E)  # shuffled, so the best ids are not the lowest
+    else:
+        hc = -(110.0 + 20.0 * e / E)
+    c = (hc / H).to(torch.bfloat16)
+    return c[:, None].expand(E, H).contiguous()
+
+
+def _extreme_tokens(regime, T, H):
+    # s_t in [1, 2) for the saturated and zero regimes, within 2.4% of 1 for
+    # the subnormal one (keeps z inside the subnormal range)
+    k = torch.arange(T, dtype=torch.float64)
+    s = 1.0 + ((k % 128) / 128.0 if regime != "subnormal" else (k % 4) / 128.0)
+    return s.to(torch.bfloat16)[:, None].expand(T, H).contiguous()
+
+
+@pytest.mark.parametrize("regime", ["saturated", "subnormal", "zero"])
+@pytest.mark.parametrize("T,via", [(12, "forward"), (37, "route"), (1500, "route"), (4100, "route")])
+def test_route_extreme_logits(T, via, regime):
+    """Logits far outside the N(0, 0.02) range, through every top-k kernel:
+    saturated scores (all 1.0: the lowest K ids, weights 1/K), subnormal scores
+    (e^z / (1 + e^z) stays nonzero below z = -88.7, where 1 / (1 + e^-z)
+    would give 0), and scores that underflow to 0 (weights 1/K, not 0/0).
+    Selection must equal the oracle's exactly (distinct logits differ by at
+    least 0.5 here), weights within the float32 precision of the scores, and
+    the layer output (forward) finite and within the bar."""
+    H, E, K = 256, 64, 6
+    router = _extreme_router(regime, E, H)
+    x = _extreme_tokens(regime, T, H)
+    wl = inputs.custom(f"extreme_{regime}", T, H, E, K, 64, 64, True, seed=2)
+    if via == "route":
+        idx, tw = api.route(api.dims_of(wl), x.cuda(), router.cuda(), None)
+    else:
+        w = {k: (v.cuda() if v is not None else None) for k, v in inputs.make_layer(wl, 0, "cpu").items()}
+        w["router"] = router.cuda()
+        out, idx, tw = api.forward(api.dims_of(wl), x.cuda(), w, return_routing=True)
+    torch.cuda.synchronize()
+    gi, gw = idx.cpu().numpy(), tw.cpu().numpy()
+    dd = G.oracle_dims(wl)
+    xh, rh = inputs.to_numpy_f32(x), inputs.to_numpy_f32(router)
+    o_idx, o_w, _ = orc.route(dd, xh, rh, None)
+    sc = orc.scores(dd, xh, rh, None)
+    np.testing.assert_array_equal(gi, o_idx)
+    assert np.all(np.isfinite(gw))
+    sel_sum = np.take_along_axis(sc.astype(np.float64), o_idx, 1).sum(1)
+    if regime == "saturated":
+        assert np.all(sc == 1.0)
+        np.testing.assert_array_equal(gi, np.tile(np.arange(K), (T, 1)))
+        np.testing.assert_array_equal(gw, np.full((T, K), np.float32(1.0 / K)))
+    elif regime == "zero":
+        assert np.all(sc == 0.0)
+        np.testing.assert_array_equal(gi, np.tile(np.arange(K), (T, 1)))
+        np.testing.assert_array_equal(gw, np.full((T, K), np.float32(1.0 / K)))
+    else:
+        assert np.all(sel_sum > 0) and np.all(sc < np.finfo(np.float32).tiny)
+        # each score is a multiple of 2^-149; one step of difference per score
+        # moves a weight by at most about 2^-149 / sum
+        tol = 3.0 * 2.0 ** -149 / sel_sum[:, None] + G.WEIGHT_TOL
+        assert np.all(np.abs(gw - o_w) <= tol), float(np.max(np.abs(gw - o_w) - tol))
+    if via == "forward":
+        ref, _, _, _ = orc.forward(dd, xh, G.host_weights(w), force_idx=gi)
+        G.check_output(out.cpu().numpy(), ref, f"extreme_{regime}")
 
 
 @pytest.mark.parametrize("name", ["decode32", "prefill4096"])
@@ -422,6 +506,8 @@ DENSE_CASES = [
     ("d_t700_f32",  700,  128,  128,  False),   # float32 large-batch kernels
     ("d_flint32",   32,   2048, 6144, True),    # the dense layer's width, decode batch (down split 8 ways)
     ("d_t20_s6",    20,   1024, 1536, True),    # down split 6 ways
+    ("d_t40_f32",   40,   256,  512,  False),   # float32 on the streaming kernels
+    ("d_t300_f32",  300,  256,  768,  False),   # float32 on the streaming kernels, down split
 ]
 
 
