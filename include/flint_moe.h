@@ -239,6 +239,28 @@ flint_status flint_dense_mlp(const flint_dense_dims *dims, int32_t T, const void
                              const void *up, const void *down, void *out, flint_dtype out_dtype, void *ws,
                              size_t ws_bytes, void *stream, void *const *events);
 
+/* ---- Allocation-free variant ----------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * flint_moe_forward with the same arguments except the workspace: the scratch
+ * lives in a file-scope device array of FLINT_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends (looked up with
+ * hipGetSymbolAddress at the first call on each device; no call allocates).
+ * Results are those of flint_moe_forward, bit for bit.
+ *   - A shape whose flint_moe_workspace_bytes(dims, T) exceeds
+ *     FLINT_STATIC_SCRATCH_BYTES is refused with FLINT_WORKSPACE_TOO_SMALL
+ *     (48 MiB: the Flint layer up to T = 750 tokens), before any launch.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *     GPU (several streams or threads at once) race and give undefined results;
+ *     serialise them, or use flint_moe_forward with a workspace per stream.
+ *   - Other errors as for flint_moe_forward; FLINT_DEVICE_ERROR also when the
+ *     array's address cannot be looked up. */
+#define FLINT_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
+
+flint_status flint_moe_forward_static(const flint_moe_dims *dims, int32_t T, const void *x,
+                                      const flint_moe_weights *weights, void *out, flint_dtype out_dtype,
+                                      int32_t *topk_idx_out, float *topk_w_out, void *stream);
+
 /* RMSNorm between stacked MoE layers (unit gain): out = bf16(in / sqrt(mean(in^2) + eps)),
  * the mean over each row of H values.  in [T][H] float32, out [T][H] bf16.
  * H must be a multiple of 64 and at most 8192.  This joins consecutive layers in

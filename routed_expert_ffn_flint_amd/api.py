@@ -159,6 +159,25 @@ def flint_moe_forward(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=No
         raise FlintError(st, "flint_moe_forward" if events is None else "flint_moe_forward_profiled")
 
 
+def flint_moe_forward_static(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=None, stream=None):
+    """flint_moe_forward without a workspace argument: the library's own static
+    device scratch (FLINT_STATIC_SCRATCH_BYTES per GPU) serves as the workspace,
+    and the call allocates nothing.  Calls that overlap on one GPU race."""
+    T = x.shape[0]
+    _check_tensor("x", x, _elem(d), (T, d.hidden))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check_tensor("out", out, None, (T, d.hidden))
+    _check_tensor("topk_idx_out", topk_idx_out, torch.int32, (T, d.top_k))
+    _check_tensor("topk_w_out", topk_w_out, torch.float32, (T, d.top_k))
+    ws_struct = weights if isinstance(weights, Weights) else weights_struct(d, weights)
+    out_dt = BF16 if out.dtype == torch.bfloat16 else F32
+    st = load().flint_moe_forward_static(ctypes.byref(d), T, _ptr(x), ctypes.byref(ws_struct), _ptr(out), out_dt,
+                                         _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream))
+    if st != OK:
+        raise FlintError(st, "flint_moe_forward_static")
+
+
 def weights_mx4_struct(d: Dims, w: dict) -> WeightsMx4:
     """MXFP4 expert weights in the tiled order of flint_moe_forward_mx4 (keys
     <name>_q codes [..., rows/16, cols/32, 16, 16] and <name>_s scales [...,

@@ -331,10 +331,11 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
     return FLINT_OK;
 }
 
-// Checks shared by both forward entry points (everything but the weights).
-static flint_status check_forward(const flint_moe_dims *d, int32_t T, const void *x, const void *router,
-                                  const float *router_bias, void *out, flint_dtype out_dtype,
-                                  int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes)
+// Checks shared by both forward entry points: everything but the weights and
+// the workspace.
+static flint_status check_forward_args(const flint_moe_dims *d, int32_t T, const void *x, const void *router,
+                                       const float *router_bias, void *out, flint_dtype out_dtype,
+                                       int32_t *topk_idx_out, float *topk_w_out)
 {
     flint_status st = check_dims(d);
     if (st != FLINT_OK) return st;
@@ -346,8 +347,45 @@ static flint_status check_forward(const flint_moe_dims *d, int32_t T, const void
     if (router_bias && !aligned16(router_bias)) return FLINT_UNSUPPORTED;
     if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
         return FLINT_UNSUPPORTED;
+    return FLINT_OK;
+}
+
+static flint_status check_forward(const flint_moe_dims *d, int32_t T, const void *x, const void *router,
+                                  const float *router_bias, void *out, flint_dtype out_dtype,
+                                  int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes)
+{
+    const flint_status st =
+        check_forward_args(d, T, x, router, router_bias, out, out_dtype, topk_idx_out, topk_w_out);
+    if (st != FLINT_OK || T == 0) return st;
     return check_ws(d, T, ws, ws_bytes);
 }
+
+// The bf16/float32 weight pointers (after check_dims).
+static flint_status check_weights(const flint_moe_dims *d, const flint_moe_weights *wt)
+{
+    if (!wt->gate || !wt->up || !wt->down) return FLINT_INVALID_ARG;
+    const bool has_shared = d->shared_inter > 0;
+    if (has_shared && (!wt->shared_gate || !wt->shared_up || !wt->shared_down)) return FLINT_INVALID_ARG;
+    if (!aligned16(wt->gate) || !aligned16(wt->up) || !aligned16(wt->down)) return FLINT_UNSUPPORTED;
+    if (has_shared && (!aligned16(wt->shared_gate) || !aligned16(wt->shared_up) || !aligned16(wt->shared_down)))
+        return FLINT_UNSUPPORTED;
+    return FLINT_OK;
+}
+
+namespace flint {
+
+// Every check flint_moe_forward makes except the workspace's (used by the
+// entry point whose workspace is the library's own static scratch).
+flint_status check_forward_call(const flint_moe_dims *d, int32_t T, const void *x, const flint_moe_weights *wt,
+                                void *out, flint_dtype out_dtype, int32_t *topk_idx_out, float *topk_w_out)
+{
+    const flint_status st = check_forward_args(d, T, x, wt ? wt->router : nullptr, wt ? wt->router_bias : nullptr,
+                                               out, out_dtype, topk_idx_out, topk_w_out);
+    if (st != FLINT_OK || T == 0) return st;
+    return check_weights(d, wt);
+}
+
+}  // namespace flint
 
 extern "C" {
 
@@ -359,12 +397,7 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     flint_status st = check_forward(d, T, x, wt ? wt->router : nullptr, wt ? wt->router_bias : nullptr, out,
                                     out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes);
     if (st != FLINT_OK || T == 0) return st;
-    if (!wt->gate || !wt->up || !wt->down) return FLINT_INVALID_ARG;
-    const bool has_shared = d->shared_inter > 0;
-    if (has_shared && (!wt->shared_gate || !wt->shared_up || !wt->shared_down)) return FLINT_INVALID_ARG;
-    if (!aligned16(wt->gate) || !aligned16(wt->up) || !aligned16(wt->down)) return FLINT_UNSUPPORTED;
-    if (has_shared && (!aligned16(wt->shared_gate) || !aligned16(wt->shared_up) || !aligned16(wt->shared_down)))
-        return FLINT_UNSUPPORTED;
+    if ((st = check_weights(d, wt)) != FLINT_OK) return st;
     ExpertArgs e{};
     e.gate = wt->gate;
     e.up = wt->up;

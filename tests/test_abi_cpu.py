@@ -210,3 +210,28 @@ def test_dense_mlp_refusals(lib):
     assert _dense(lib, dd, 32, ws_bytes=n32 - 1) == api.WORKSPACE_TOO_SMALL
     assert _dense(lib, dd, 32, ws=FAKE_WS + 16) == api.UNSUPPORTED  # 256-byte aligned workspace
     assert _dense(lib, dd, 32, ws=None) == api.INVALID_ARG
+
+
+def _forward_static(lib, d, T, x=FAKE, w=None, out=FAKE, out_dtype=api.F32):
+    w = w or _lib.Weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    return lib.flint_moe_forward_static(ctypes.byref(d), T, x, ctypes.byref(w), out, out_dtype, None, None, None)
+
+
+def test_forward_static_refusals(lib):
+    """The allocation-free entry point refuses on the host, before it looks up
+    its device scratch: the same argument errors as flint_moe_forward, and any
+    shape whose workspace would exceed the static scratch."""
+    d = flint_dims()
+    assert _forward_static(lib, d, -1) == api.INVALID_ARG
+    assert _forward_static(lib, d, 0) == api.OK
+    assert _forward_static(lib, d, 32, x=None) == api.INVALID_ARG
+    assert _forward_static(lib, d, 32, x=FAKE + 2) == api.UNSUPPORTED
+    assert _forward_static(lib, flint_dims(top_k=9), 32) == api.UNSUPPORTED
+    no_gate = _lib.Weights(FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert _forward_static(lib, d, 32, w=no_gate) == api.INVALID_ARG
+    limit = 48 << 20  # FLINT_STATIC_SCRATCH_BYTES
+    assert re.search(r"FLINT_STATIC_SCRATCH_BYTES \(\(size_t\)48 << 20\)", open(HEADER).read())
+    T_max = max(T for T in range(1, 2048) if api.flint_moe_workspace_bytes(d, T) <= limit)
+    assert T_max >= 512  # the decode batches and the 256-token stack fit
+    assert _forward_static(lib, d, T_max + 1) == api.WORKSPACE_TOO_SMALL
+    assert _forward_static(lib, d, 100_000) == api.WORKSPACE_TOO_SMALL
