@@ -24,17 +24,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the Flint MoE library needs ROCm's hipcc to build")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library.  Always
-    recompiles (the build is a few tens of seconds)."""
-    out_dir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, extra_flags=(), lib: str = LIB) -> str:
+    """Compile every source for gfx950 and link the shared library at ``lib``
+    (hipcc ``extra_flags`` added to every compile).  Always recompiles (the
+    build is a few tens of seconds)."""
+    out_dir = os.path.join(os.path.dirname(os.path.abspath(lib)), "_build")
     os.makedirs(out_dir, exist_ok=True)
     common = [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # keep the backend from forming packed fp32 instructions by itself
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function", f"-I{os.path.join(HERE, '..', 'include')}",
-    ]
+    ] + list(extra_flags)
     def compile_one(src):
         obj = os.path.join(out_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
@@ -54,13 +55,13 @@ def build(verbose: bool = False) -> str:
     jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
     with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
         objs = list(pool.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = f"{lib}.tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
