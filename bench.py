@@ -59,6 +59,7 @@ KERNEL_SOURCES = {
     "k_expert_stream": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream.hip"],
     "k_expert_stream_mx4": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream_mx4.hip"],
     "k_tiled": ["common.hpp", "gemm_core.hpp", "launch.hpp", "tiled.hip"],
+    "k_fused_decode": ["common.hpp", "gemm_core.hpp", "launch.hpp", "topk.hpp", "fused.hip"],
 }
 # largest bf16 batches the library serves with the streaming kernels (a MoE
 # layer, a dense layer); larger ones go to the tiled kernels
@@ -76,6 +77,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true", help="replay the steps from a captured HIP graph")
+    p.add_argument("--fused", action="store_true",
+                   help="the layer through flint_moe_forward_fused (top-k through down in one persistent kernel; "
+                        "bf16 batches of up to 64 tokens)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for the HBM "
                         "byte counters) and exit")
@@ -489,6 +493,9 @@ def main():
         if wl.mx4:
             st = lib.flint_moe_forward_mx4(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp,
                                            wsp, wsn, sp, arr)
+        elif args.fused:
+            st = lib.flint_moe_forward_fused(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp,
+                                             wsp, wsn, sp, arr)
         elif events is None:
             st = lib.flint_moe_forward(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp, wsp, wsn, sp)
         else:
@@ -584,6 +591,8 @@ def main():
         step(i, ev_sets[i])
     torch.cuda.synchronize()
     names = ["router", "topk_dispatch", "gate_up", "down", "combine"]
+    if args.fused:  # stage 1 is the fused kernel (top-k through down); stages 2 and 3 are empty
+        names = ["router", "fused", "_empty2", "_empty3", "combine"]
     stage = {n: [] for n in names}
     for i in range(n_prof):
         for evs in ev_sets[i]:
@@ -592,7 +601,7 @@ def main():
     for sets in ev_sets:
         for evs in sets:
             hev.destroy(evs)
-    stage_us = {n: float(np.mean(v) * 1e3) for n, v in stage.items()}
+    stage_us = {n: float(np.mean(v) * 1e3) for n, v in stage.items() if not n.startswith("_")}
 
     # algorithmic figures averaged over the copies the steps used
     avg = lambda key: float(np.mean([p[key] for p in per_copy]))  # noqa: E731
@@ -602,9 +611,15 @@ def main():
     gu_flops = float(np.mean([p["flops"]["gate_up"] for p in per_copy]))
     big = gu_flops / gate_up_bytes >= RIDGE  # arithmetic intensity of the gate/up kernel
     kernel = "k_expert_stream_mx4" if wl.mx4 else ("k_expert_stream" if T <= STREAM_MAX_T else "k_tiled")
+    kname = f"{kernel}<gate/up> (grouped gate/up GEMM + SwiGLU, routed and shared)"
+    if args.fused:
+        # the dominant kernel is the fused one: the gate/up and the down bytes
+        kernel = "k_fused_decode"
+        kname = "k_fused_decode (top-k, dispatch, gate/up + SwiGLU, down)"
+        gate_up_bytes = avg("gate_up_bytes") + avg("down_bytes")
+        stage_us["gate_up"] = stage_us["fused"]
     digest = sources_digest(kernel)
     traffic = counters_traffic(kernel, wl.name, digest)
-    kname = f"{kernel}<gate/up> (grouped gate/up GEMM + SwiGLU, routed and shared)"
     if big:
         achieved = gu_flops / (stage_us["gate_up"] * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -631,7 +646,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {'47 stacked' if stack else 'one'} Flint MoE layer(s), T={T}, "
                                f"H={wl.hidden}, E={wl.n_experts} top-{wl.top_k}, I={wl.inter}, "
-                               f"Is={wl.shared_inter}" + (", expert weights MXFP4" if wl.mx4 else ""),
+                               f"Is={wl.shared_inter}" + (", expert weights MXFP4" if wl.mx4 else "")
+                               + (", fused decode kernel" if args.fused else ""),
                    "T": T, "weight_copies": n_copies,
                    "graph": bool(graph is not None), "wall_s": wall},
         "roofline": roofline,

@@ -163,6 +163,28 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *dims, int32_t T, c
                                         float *topk_w_out, void *ws, size_t ws_bytes, void *stream,
                                         void *const *events);
 
+/* ---- Persistent fused decode ------------------------------------------------
+ * The layer with top-k, dispatch, gate/up + SwiGLU and down in one persistent
+ * launch between the router and the combine (release news page, "Built with
+ * the Eureka Machine": a megakernel that fuses the decode forward pass; the
+ * same idea for this layer).  The expert work runs as data flow: a unit's down
+ * items wait only for that unit's gate/up items, through completion counters
+ * in the workspace; no wait can deadlock (items are claimed in dependency
+ * order), and every wait is bounded: one that gives up makes every output NaN.
+ * Same arguments, workspace size and results as flint_moe_forward_profiled
+ * (the same bits: the expert items are those flint_moe_forward runs at these
+ * sizes); in `events` stage 1 covers the fused kernel and stages 2 and 3 are
+ * empty.  Supported: dims.dtype BF16, 1 <= T <= 64, H and I multiples of 256,
+ * Is a multiple of I with Is / I <= 8; anything else is FLINT_UNSUPPORTED.
+ * flint_moe_forward does not use it: measured on one MI355X at T = 32 (the
+ * Flint layer), the separate kernels take 178 us a layer and this path
+ * 196-203 us (its top-k -> dispatch chain costs ~16 us before routed weights
+ * stream, with only the shared expert to overlap it). */
+flint_status flint_moe_forward_fused(const flint_moe_dims *dims, int32_t T, const void *x,
+                                     const flint_moe_weights *weights, void *out, flint_dtype out_dtype,
+                                     int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                                     void *stream, void *const *events);
+
 /* ---- Expert weights in MXFP4 (block-scaled 4-bit) --------------------------
  * The pages' low-bit builds store weights in 4 bits ("Recursive launches
  * Flint: open-weight coding model with 39.8 billion parameters for local

@@ -159,6 +159,33 @@ def flint_moe_forward(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=No
         raise FlintError(st, "flint_moe_forward" if events is None else "flint_moe_forward_profiled")
 
 
+def flint_moe_forward_fused(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=None, ws=None, stream=None,
+                            events=None):
+    """The layer through the persistent fused decode kernel (bf16, up to 64
+    tokens; see include/flint_moe.h); arguments as flint_moe_forward, events
+    None or 10 hipEvent_t handles."""
+    T = x.shape[0]
+    _check_tensor("x", x, _elem(d), (T, d.hidden))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check_tensor("out", out, None, (T, d.hidden))
+    _check_tensor("topk_idx_out", topk_idx_out, torch.int32, (T, d.top_k))
+    _check_tensor("topk_w_out", topk_w_out, torch.float32, (T, d.top_k))
+    _check_tensor("ws", ws, torch.uint8)
+    ws_struct = weights if isinstance(weights, Weights) else weights_struct(d, weights)
+    out_dt = BF16 if out.dtype == torch.bfloat16 else F32
+    arr = None
+    if events is not None:
+        if len(events) != 10:
+            raise ValueError("events: 10 hipEvent_t handles (start/stop of 5 stages)")
+        arr = (ctypes.c_void_p * 10)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
+    st = load().flint_moe_forward_fused(ctypes.byref(d), T, _ptr(x), ctypes.byref(ws_struct), _ptr(out), out_dt,
+                                        _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream), arr)
+    if st != OK:
+        raise FlintError(st, "flint_moe_forward_fused")
+
+
 def flint_moe_forward_static(d: Dims, x, weights, out, topk_idx_out=None, topk_w_out=None, stream=None):
     """flint_moe_forward without a workspace argument: the library's own static
     device scratch (FLINT_STATIC_SCRATCH_BYTES per GPU) serves as the workspace,
@@ -283,8 +310,10 @@ def flint_rmsnorm(inp, out, eps=1e-6, stream=None):
 
 # ---- convenience: allocate outputs with torch, then call the entry points ----
 
-def forward(d: Dims, x, weights, out_dtype=torch.float32, ws=None, stream=None, return_routing=False):
-    """The layer; MXFP4 weight dicts (keys ending in _q/_s) go to flint_moe_forward_mx4."""
+def forward(d: Dims, x, weights, out_dtype=torch.float32, ws=None, stream=None, return_routing=False,
+            fused=False):
+    """The layer; MXFP4 weight dicts (keys ending in _q/_s) go to flint_moe_forward_mx4,
+    fused=True to flint_moe_forward_fused."""
     T = x.shape[0]
     out = torch.empty((T, d.hidden), dtype=out_dtype, device=x.device)
     idx = torch.empty((T, d.top_k), dtype=torch.int32, device=x.device) if return_routing else None
@@ -293,6 +322,8 @@ def forward(d: Dims, x, weights, out_dtype=torch.float32, ws=None, stream=None, 
         ws = workspace(d, T, x.device)
     if isinstance(weights, WeightsMx4) or (isinstance(weights, dict) and "gate_q" in weights):
         flint_moe_forward_mx4(d, x, weights, out, idx, tw, ws, stream)
+    elif fused:
+        flint_moe_forward_fused(d, x, weights, out, idx, tw, ws, stream)
     else:
         flint_moe_forward(d, x, weights, out, idx, tw, ws, stream)
     return (out, idx, tw) if return_routing else out

@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libflint_moe.so")
-SOURCES = ["route.hip", "expert.hip", "stream.hip", "stream_mx4.hip", "tiled.hip", "abi.cpp", "static_ws.hip"]
+SOURCES = ["route.hip", "expert.hip", "stream.hip", "stream_mx4.hip", "tiled.hip", "fused.hip", "abi.cpp",
+           "static_ws.hip"]
 ARCH = "gfx950"
 
 

@@ -110,6 +110,10 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     w.h_shared = take((size_t)T * Is * eb);
     w.y_sorted = (float *)take(TK * H * 4);
     w.y_shared = (float *)take((size_t)shared_splits * T * H * 4);
+    if (eb == 2 && K > 0 && T <= kFusedMaxT) {  // the fused decode kernel's own state
+        w.topk_q = (int32_t *)take((size_t)kFusedQueues * TK * 4);
+        w.sync = (int32_t *)take((size_t)kFusedSyncWords * 4);
+    }
     w.bytes = off;
     return w;
 }
@@ -123,8 +127,16 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
 #ifndef FLINT_MOE_SHARED_SPLIT_T
 #define FLINT_MOE_SHARED_SPLIT_T 64
 #endif
-int moe_shared_splits(const flint_moe_dims *d, int32_t T, bool mx4)
+static bool fused_ok(const flint_moe_dims *d, int32_t T)
 {
+    return fused_eligible(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter, d->dtype == FLINT_BF16);
+}
+
+// fused: the layer runs on the fused decode kernel, which cuts the shared
+// expert into Is / I slices
+int moe_shared_splits(const flint_moe_dims *d, int32_t T, bool mx4, bool fused = false)
+{
+    if (fused) return d->shared_inter > 0 ? d->shared_inter / d->inter : 1;
     if (T > FLINT_MOE_SHARED_SPLIT_T || mx4 || d->shared_inter <= d->inter || d->shared_inter % d->inter) return 1;
     const int s = d->shared_inter / d->inter;
     if (s > 8) return 1;
@@ -154,8 +166,11 @@ const char *flint_status_string(flint_status s)
 size_t flint_moe_workspace_bytes(const flint_moe_dims *d, int32_t T)
 {
     if (check_dims(d) != FLINT_OK || check_T(d, T) != FLINT_OK) return 0;
+    // room for every path a forward call of this shape may take
+    int splits = moe_shared_splits(d, T, false);
+    if (fused_ok(d, T)) splits = std::max(splits, moe_shared_splits(d, T, false, true));
     return plan_workspace(nullptr, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
-                          elem_bytes(d), moe_shared_splits(d, T, false))
+                          elem_bytes(d), splits)
         .bytes;
 }
 
@@ -270,11 +285,11 @@ flint_status flint_moe_forward(const flint_moe_dims *d, int32_t T, const void *x
 static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void *x, const void *router,
                                  const float *router_bias, ExpertArgs e, void *out, flint_dtype out_dtype,
                                  int32_t *topk_idx_out, float *topk_w_out, void *ws, void *stream,
-                                 void *const *events)
+                                 void *const *events, bool fused = false)
 {
     hipStream_t s = (hipStream_t)stream;
     const bool bf16 = d->dtype == FLINT_BF16;
-    const int shared_splits = moe_shared_splits(d, T, e.mx4);
+    const int shared_splits = moe_shared_splits(d, T, e.mx4, fused);
     Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
                                  elem_bytes(d), shared_splits);
     // stage marks: router, top-k + dispatch, gate/up, down, combine
@@ -283,9 +298,46 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
         for (int i = 0; i < 5; ++i) marks[i] = Marks{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]};
     const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
                                                d->dtype == FLINT_BF16);
-    if (launch_router_logits(bf16, x, T, d->hidden, router, router_bias, d->n_experts, w.logits, s, marks[0]) !=
-        hipSuccess)
+    if (launch_router_logits(bf16, x, T, d->hidden, router, router_bias, d->n_experts, w.logits, s, marks[0],
+                             fused ? w.sync : nullptr, fused ? kFusedSyncWords : 0) != hipSuccess)
         return FLINT_DEVICE_ERROR;
+    if (fused) {
+        // top-k, dispatch, gate/up and down in one launch (stage marks: the
+        // kernel is stage 1; stages 2 and 3 are empty), then the combine
+        e.bf16 = true;
+        e.T = T;
+        e.H = d->hidden;
+        e.E = d->n_experts;
+        e.K = d->top_k;
+        e.I = d->inter;
+        e.Is = d->shared_inter;
+        e.x = x;
+        e.sorted_token = w.sorted_token;
+        e.offsets = w.offsets;
+        e.slot_of = w.slot_of;
+        e.topk_w = topk_w_out ? topk_w_out : w.topk_w;
+        e.h_sorted = w.h_sorted;
+        e.h_shared = w.h_shared;
+        e.y_sorted = w.y_sorted;
+        e.y_shared = w.y_shared;
+        e.shared_splits = shared_splits;
+        e.out = out;
+        e.out_bf16 = out_dtype == FLINT_BF16;
+        e.tiles = tiles;
+        e.cus = device_cus();
+        e.fail = w.sync + (2 * kFusedQueues + kMaxExperts + kFusedMaxShared) * 32;
+        if (launch_fused_decode(e, w.logits, router_splits(T, d->hidden, d->n_experts, bf16),
+                                topk_idx_out ? topk_idx_out : w.topk_idx, const_cast<float *>(e.topk_w), w.topk_q,
+                                w.sync, w.counts, w.offsets, w.sorted_token, w.slot_of, s,
+                                Marks{marks[1].start, marks[1].stop}) != hipSuccess)
+            return FLINT_DEVICE_ERROR;
+        for (int i = 2; i <= 3; ++i) {
+            if (marks[i].start && hipEventRecord(marks[i].start, s) != hipSuccess) return FLINT_DEVICE_ERROR;
+            if (marks[i].stop && hipEventRecord(marks[i].stop, s) != hipSuccess) return FLINT_DEVICE_ERROR;
+        }
+        if (launch_combine(e, s, marks[4]) != hipSuccess) return FLINT_DEVICE_ERROR;
+        return FLINT_OK;
+    }
 
     DispatchArgs a = dispatch_args(d, T, w);
     if (e.mx4) {
@@ -407,6 +459,26 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
     e.shared_down = wt->shared_down;
     return launch_layer(d, T, x, wt->router, wt->router_bias, e, out, out_dtype, topk_idx_out, topk_w_out, ws,
                         stream, events);
+}
+
+flint_status flint_moe_forward_fused(const flint_moe_dims *d, int32_t T, const void *x, const flint_moe_weights *wt,
+                                     void *out, flint_dtype out_dtype, int32_t *topk_idx_out, float *topk_w_out,
+                                     void *ws, size_t ws_bytes, void *stream, void *const *events)
+{
+    flint_status st = check_forward(d, T, x, wt ? wt->router : nullptr, wt ? wt->router_bias : nullptr, out,
+                                    out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes);
+    if (st != FLINT_OK || T == 0) return st;
+    if ((st = check_weights(d, wt)) != FLINT_OK) return st;
+    if (!fused_ok(d, T)) return FLINT_UNSUPPORTED;
+    ExpertArgs e{};
+    e.gate = wt->gate;
+    e.up = wt->up;
+    e.down = wt->down;
+    e.shared_gate = wt->shared_gate;
+    e.shared_up = wt->shared_up;
+    e.shared_down = wt->shared_down;
+    return launch_layer(d, T, x, wt->router, wt->router_bias, e, out, out_dtype, topk_idx_out, topk_w_out, ws,
+                        stream, events, true);
 }
 
 flint_status flint_moe_forward_mx4(const flint_moe_dims *d, int32_t T, const void *x,

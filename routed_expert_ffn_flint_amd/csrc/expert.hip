@@ -291,6 +291,10 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
             acc[3] += v[3];
         }
     }
+    if (a.fail && *a.fail) {  // a wait of the fused decode kernel gave up: the result is void
+        const float nan = __builtin_nanf("");
+        acc = f32x4{nan, nan, nan, nan};
+    }
     if (a.out_bf16) {
         uint16_t *o = (uint16_t *)a.out + (size_t)t * H + c;
         o[0] = f32_to_bf16(acc[0]);
@@ -360,6 +364,12 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
         err = launch_k(k_down<DT, 4, 4, 1, 4, false>, g2, 256, 0, stream, m2, a, ns2);
     if (err != hipSuccess) return err;
     return a.skip_combine ? hipSuccess : launch_k(k_combine, gc, 256, 0, stream, m3, a);
+}
+
+hipError_t launch_combine(const ExpertArgs &a, hipStream_t stream, Marks m)
+{
+    if (a.T <= 0) return hipSuccess;
+    return launch_k(k_combine, dim3(a.T, (a.H + 1023) / 1024), 256, 0, stream, m, a);
 }
 
 hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks)

@@ -60,6 +60,13 @@ constexpr int kStreamMaxT = 512;
 constexpr int kTiledFromT = FLINT_TILED_FROM_T;
 constexpr int kDenseTiledFromT = FLINT_DENSE_TILED_FROM_T;
 
+// The persistent fused decode kernel (fused.hip): queues (work-group classes),
+// largest batch, most shared-expert slices, and its counter words.
+constexpr int kFusedQueues = 8;
+constexpr int kFusedMaxT = 64;
+constexpr int kFusedMaxShared = 8;
+constexpr int kFusedSyncWords = (2 * kFusedQueues + kMaxExperts + kFusedMaxShared + 1) * 32;
+
 // Tile shapes of the expert kernels for one launch regime.
 struct ExpertTiles {
     int bm1;  // rows per gate/up tile
@@ -94,6 +101,8 @@ struct Workspace {
     void *h_shared;       // [T][Is] dtype
     float *y_sorted;      // [T*K][H]
     float *y_shared;      // [T][H]
+    int32_t *topk_q;      // fused decode: [queues][T][K] per-queue copies of the selection
+    int32_t *sync;        // fused decode: kFusedSyncWords counters
     size_t bytes;         // total bytes needed
 };
 
@@ -119,8 +128,11 @@ int small_router_splits(int T, int H, int E);
 
 // logits[t][e] = x[t] . router[e] (+ bias[e]), float32, as router_splits
 // partial arrays (bias in the first) that sum to it.
+// zero / nzero: int32 words the kernel also sets to 0 (the fused decode
+// kernel's counters; T < 1024 only), or null.
 hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const void *router,
-                                const float *bias, int E, float *logits, hipStream_t stream, Marks m = {});
+                                const float *bias, int E, float *logits, hipStream_t stream, Marks m = {},
+                                int32_t *zero = nullptr, int nzero = 0);
 
 // Top-k selection and/or dispatch.  See route.hip for the modes.
 struct DispatchArgs {
@@ -161,6 +173,7 @@ struct ExpertArgs {
     bool skip_combine;  // the shared down stage writes the output itself (a dense layer, float32 out)
     ExpertTiles tiles;
     int cus;  // compute units of the device (sizes the persistent kernels' grids)
+    const int32_t *fail;  // nonzero: a bounded wait of the fused decode kernel gave up (combine writes NaN)
 };
 // marks (nullable): 3 stages, gate/up (+ shared), down (+ shared), combine.
 hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks);
@@ -199,6 +212,15 @@ bool tiled_router_eligible(int T, int H, bool bf16);
 constexpr int kRouterSplits = FLINT_ROUTER_SPLITS;
 hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
                                float *logits, hipStream_t stream, Marks m);
+
+// The fused decode kernel (top-k, dispatch, gate/up, down in one launch) for
+// bf16 batches of up to kFusedMaxT tokens: eligibility and launch.  The
+// combine (launch_combine) follows it.
+bool fused_eligible(int T, int H, int E, int K, int I, int Is, bool bf16);
+hipError_t launch_fused_decode(const ExpertArgs &a, const float *logits, int logit_splits, int32_t *topk_idx,
+                               float *topk_w, int32_t *topk_q, int32_t *sync, int32_t *counts, int32_t *offsets,
+                               int32_t *sorted_token, int32_t *slot_of, hipStream_t stream, Marks m);
+hipError_t launch_combine(const ExpertArgs &a, hipStream_t stream, Marks m);
 
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t value, hipStream_t stream);
 

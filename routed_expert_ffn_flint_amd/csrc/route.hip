@@ -42,6 +42,7 @@
 
 #include "gemm_core.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace flint {
 
@@ -52,11 +53,17 @@ namespace flint {
 // latency of reading the 1 MiB router matrix matters more than reuse).
 // SPLIT == 1: 4 waves in a 2x2 grid, each (MB*16) tokens x (NB*16) experts
 // over all of H.
+// zero / nzero: words to set to 0 besides (the fused decode kernel's counters).
 template <typename DT, int MB, int NB, int SPLIT>
 __global__ __launch_bounds__(SPLIT > 1 ? SPLIT * 64 : 256) void k_router_logits(
     const typename DT::storage *__restrict__ x, int T, int H, const typename DT::storage *__restrict__ router,
-    const float *__restrict__ bias, int E, float *__restrict__ z)
+    const float *__restrict__ bias, int E, float *__restrict__ z, int32_t *__restrict__ zero, int nzero)
 {
+    if (zero) {
+        const int nthreads = gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+        const int id = ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+        for (int i = id; i < nzero; i += nthreads) zero[i] = 0;
+    }
     using S = typename DT::storage;
     constexpr bool SPLITK = SPLIT > 1;
     constexpr int WM = SPLITK ? 1 : 2, WN = SPLITK ? 1 : 2;
@@ -137,10 +144,14 @@ int small_router_splits(int T, int H, int E)
 }
 
 hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const void *router,
-                                const float *bias, int E, float *logits, hipStream_t stream, Marks m)
+                                const float *bias, int E, float *logits, hipStream_t stream, Marks m,
+                                int32_t *zero, int nzero)
 {
     if (T <= 0) return hipSuccess;
-    if (tiled_router_eligible(T, H, bf16)) return launch_router_tiled(x, T, H, router, bias, E, logits, stream, m);
+    if (tiled_router_eligible(T, H, bf16)) {
+        if (zero) return hipErrorInvalidValue;  // (the counters belong to batches below 1024 tokens)
+        return launch_router_tiled(x, T, H, router, bias, E, logits, stream, m);
+    }
     const uint16_t *xb = (const uint16_t *)x, *rb = (const uint16_t *)router;
     const float *xf = (const float *)x, *rf = (const float *)router;
     if (T < 1024) {
@@ -151,8 +162,10 @@ hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const vo
         dim3 grid((E + 15) / 16, (T + 15) / 16, zs);
         const int thr = 1024 / zs;
 #define FLINT_ROUTER_LAUNCH(W)                                                                              \
-    return bf16 ? launch_k(k_router_logits<BF16, 1, 1, W>, grid, thr, 0, stream, m, xb, T, H, rb, bias, E, logits) \
-                : launch_k(k_router_logits<F32, 1, 1, W>, grid, thr, 0, stream, m, xf, T, H, rf, bias, E, logits)
+    return bf16 ? launch_k(k_router_logits<BF16, 1, 1, W>, grid, thr, 0, stream, m, xb, T, H, rb, bias, E, logits, \
+                           zero, nzero)                                                                        \
+                : launch_k(k_router_logits<F32, 1, 1, W>, grid, thr, 0, stream, m, xf, T, H, rf, bias, E, logits, \
+                           zero, nzero)
         switch (zs) {
         case 2: FLINT_ROUTER_LAUNCH(8);
         case 4: FLINT_ROUTER_LAUNCH(4);
@@ -162,8 +175,11 @@ hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const vo
 #undef FLINT_ROUTER_LAUNCH
     }
     dim3 grid((E + 127) / 128, (T + 63) / 64);
-    if (bf16) return launch_k(k_router_logits<BF16, 2, 4, 1>, grid, 256, 0, stream, m, xb, T, H, rb, bias, E, logits);
-    return launch_k(k_router_logits<F32, 2, 4, 1>, grid, 256, 0, stream, m, xf, T, H, rf, bias, E, logits);
+    if (bf16)
+        return launch_k(k_router_logits<BF16, 2, 4, 1>, grid, 256, 0, stream, m, xb, T, H, rb, bias, E, logits, zero,
+                        nzero);
+    return launch_k(k_router_logits<F32, 2, 4, 1>, grid, 256, 0, stream, m, xf, T, H, rf, bias, E, logits, zero,
+                    nzero);
 }
 
 // ---------------------------------------------------------------------------
@@ -230,27 +246,6 @@ __device__ int finish_offsets_and_lists(int c, int E, int32_t *offsets, int32_t 
         meta[1] = tot2;
     }
     return off;  // expert threadIdx.x's first slot
-}
-
-// sigmoid(z) in float32.  For z < 0 it is e^z / (1 + e^z): 1 / (1 + e^-z)
-// would overflow e^-z to infinity below z = -88.7 and return 0, where the
-// score is still a float32 subnormal (it reaches 0 only below about -103.3).
-__device__ __forceinline__ float score_from_logit(float z)
-{
-    if (z < 0.0f) {
-        const float e = expf(z);
-        return e / (1.0f + e);
-    }
-    return 1.0f / (1.0f + expf(-z));
-}
-
-// Routing weight of a selected expert: score / sum of the selected scores,
-// the sum in double.  When every selected score is zero (every logit below
-// about -103.3) the quotient is 0/0; each expert then gets 1/K, the share
-// equal scores get.
-__device__ __forceinline__ float routing_weight(float s, double sum, int K)
-{
-    return sum > 0.0 ? (float)((double)s / sum) : (float)(1.0 / K);
 }
 
 // Selection key of a candidate: larger key = selected first.  Scores are
@@ -448,79 +443,20 @@ __device__ __forceinline__ void write_topk(const uint64_t (&l)[kMaxTopK], int t,
         }
 }
 
-// Top-K of one token by one wave (E <= 256: four candidates per lane, expert
-// lane + 64*i), by a bitwise search for the K-th largest score: float32 scores
-// are >= 0, so their bit patterns order like the values, and the K-th largest
-// pattern is the largest v with at least K patterns >= v, found one bit at a
-// time from the top with wave-wide counts (ballots).  Then every score above
-// it is selected, and of those equal to it the lowest expert indices up to K
-// (with an early stop, the prefix found instead: see below).
-// A chain of ~32 short compare/count steps instead of log2(64) merges of
-// sorted 8-entry lists.  Writes topk_idx (ascending ids) and topk_w (s over
-// the sum of the K selected, the sum in double in ascending id order).
+// Top-K of one token by one wave (wave_topk_select), written out: topk_idx
+// (ascending ids) and topk_w, and for a one-tile batch the selection in LDS.
 __device__ __forceinline__ void wave_topk(const float *zt, size_t split_stride, int nsplit, int E, int K, int t,
                                           int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
                                           float *ls, int *le, int16_t *sel_lds = nullptr)
 {
     const int lane = threadIdx.x & 63;
-    uint32_t u[4];
-    bool v[4];
-    float z[4];
-    // every load unconditional (experts past E read expert 0 and are masked),
-    // so the four go out together instead of one latency each
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E;
-        z[i] = zt[v[i] ? e : 0];
-    }
-    for (int sp = 1; sp < nsplit; ++sp)  // partial sums, in order
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] += zt[sp * split_stride + (v[i] ? lane + 64 * i : 0)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = v[i] ? __float_as_uint(score_from_logit(z[i])) : 0u;
-    // (bit 31, the sign, is 0 in every score.)  Once exactly K patterns are
-    // >= the prefix, those K are the selection: the loop stops there (the
-    // count is wave-uniform), typically after half the bits.
-    uint32_t thr = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(v[i] && u[i] >= cand));
-        if (cnt >= K) {
-            thr = cand;
-            if (cnt == K) break;
-        }
-    }
-    int gt = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(v[i] && u[i] > thr));
-    const int need = K - gt;  // taken from the scores equal to thr, lowest ids first
-    int eq_before = 0, sel_before = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint64_t eq = __ballot(v[i] && u[i] == thr);
-        const int eq_rank = eq_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32),
-                                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
-        const bool sel = v[i] && (u[i] > thr || (u[i] == thr && eq_rank < need));
-        const uint64_t sm = __ballot(sel);
-        if (sel) {
-            const int r = sel_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
-            ls[r] = __uint_as_float(u[i]);
-            le[r] = lane + 64 * i;
-        }
-        eq_before += __popcll(eq);
-        sel_before += __popcll(sm);
-    }
-    __builtin_amdgcn_wave_barrier();
-    double sum = 0.0;
-    for (int k = 0; k < K; ++k) sum += (double)ls[k];
+    int idx;
+    float w;
+    wave_topk_select(zt, split_stride, nsplit, E, K, ls, le, idx, w);
     if (lane < K) {
-        topk_idx[(size_t)t * K + lane] = le[lane];
-        topk_w[(size_t)t * K + lane] = routing_weight(ls[lane], sum, K);
-        if (sel_lds) sel_lds[t * K + lane] = (int16_t)le[lane];  // (a one-tile batch: t is tile-relative)
+        topk_idx[(size_t)t * K + lane] = idx;
+        topk_w[(size_t)t * K + lane] = w;
+        if (sel_lds) sel_lds[t * K + lane] = (int16_t)idx;  // (a one-tile batch: t is tile-relative)
     }
 }
 

@@ -235,3 +235,20 @@ def test_forward_static_refusals(lib):
     assert T_max >= 512  # the decode batches and the 256-token stack fit
     assert _forward_static(lib, d, T_max + 1) == api.WORKSPACE_TOO_SMALL
     assert _forward_static(lib, d, 100_000) == api.WORKSPACE_TOO_SMALL
+
+
+def test_forward_fused_refusals(lib):
+    """The fused decode entry point takes bf16 batches of 1..64 tokens with H and
+    I multiples of 256 and Is a multiple of I (at most 8 of them); it refuses
+    anything else on the host, after the checks flint_moe_forward makes."""
+    def call(d, T):
+        w = _lib.Weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+        return lib.flint_moe_forward_fused(ctypes.byref(d), T, FAKE, ctypes.byref(w), FAKE, api.F32, None, None,
+                                           FAKE_WS, 1 << 30, None, None)
+    assert call(flint_dims(), -1) == api.INVALID_ARG
+    assert call(flint_dims(), 0) == api.OK
+    assert call(flint_dims(), 65) == api.UNSUPPORTED
+    assert call(flint_dims(dtype=api.F32), 32) == api.UNSUPPORTED
+    assert call(flint_dims(hidden=128), 32) == api.UNSUPPORTED
+    assert call(flint_dims(inter=192, shared_inter=0), 32) == api.UNSUPPORTED
+    assert call(flint_dims(shared_inter=768), 32) == api.UNSUPPORTED  # not a multiple of I = 512

@@ -61,11 +61,45 @@ SMALL = [
     ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
     ("t2100_big", 2100, 256, 16, 4, 128, 128, True, True),   # 256-row tiles, router split over H
     ("t5000_ns",  5000, 128, 8,  2, 128, 0,   True, False),  # 256-row tiles, no shared expert
+    # the fused decode kernel (bf16, T <= 64, H and I multiples of 256, Is a multiple of I)
+    ("fz_t7",       7,   512, 24, 3, 256, 512, True, True),
+    ("fz_t1_k1",    1,   256, 8,  1, 256, 256, True, False),
+    ("fz_t64_k8",   64,  1024, 64, 8, 256, 0,  True, False),   # no shared expert, every queue busy
+    ("fz_t40_e200", 40,  768, 200, 6, 512, 1024, True, True),  # E not a multiple of 16, H = 3 x 256
+    ("fz_t19_s4",   19,  512, 32, 4, 256, 1024, True, False),  # four shared slices
+    ("fz_t2_e256",  2,   2048, 256, 6, 512, 1024, True, False),  # most queues hold one unit or none
     # float32 layers on the weight-streaming kernels (H, I, Is multiples of 256)
     ("t40_f32_st",  40,  256, 16, 2, 256, 512, False, False),
     ("t200_f32_st", 200, 512, 32, 6, 256, 256, False, True),
     ("t512_f32_st", 512, 256, 16, 4, 256, 256, False, False),  # the largest float32 streaming batch
 ]
+
+
+FUSED = [c for c in SMALL if c[0].startswith("fz_")] + [
+    # name,      T,  H,    E,   K, I,   Is,   bf16, bias
+    ("fz_flint1",  1,  2048, 256, 6, 512, 1024, True, False),
+    ("fz_flint8",  8,  2048, 256, 6, 512, 1024, True, True),
+    ("fz_flint32", 32, 2048, 256, 6, 512, 1024, True, False),
+    ("fz_flint64", 64, 2048, 256, 6, 512, 1024, True, False),  # the largest fused batch
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_fused_entry_point_equals_forward(case):
+    """flint_moe_forward_fused (top-k through down in one persistent kernel)
+    gives flint_moe_forward's bits (routing and outputs), and those are the
+    oracle's on every token."""
+    name, T, H, E, K, I, Is, bf16, bias = case
+    wl = inputs.custom(name, T, H, E, K, I, Is, bf16, seed=6, zipf=bias)
+    w, x = _layer(wl)
+    d = api.dims_of(wl)
+    ref = api.forward(d, x, w, return_routing=True)
+    got = api.forward(d, x, w, return_routing=True, fused=True)
+    torch.cuda.synchronize()
+    for r, g, what in zip(ref, got, ("out", "topk_idx", "topk_w")):
+        assert torch.equal(r.view(torch.uint8), g.view(torch.uint8)), f"{name}: fused {what} differs"
+    st = G.parity_full(wl, w, x)
+    print(f"{name}: fused == forward, rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
@@ -684,6 +718,49 @@ def test_graph_replays_match_eager(case):
         torch.cuda.synchronize()
         for o, ref in zip(outs, refs):
             assert torch.equal(o.view(torch.uint8), ref.view(torch.uint8)), f"{name} T={T}: replay {r} differs"
+
+
+def test_fused_graph_replays_and_concurrent_calls():
+    """The fused entry point captured in a HIP graph and replayed (a dirty
+    workspace before each replay) equals its eager result bit for bit; and two
+    fused calls running at once on two streams (their persistent grids then
+    share the GPU, so not every work-group is resident at first) both finish
+    with their eager results."""
+    wl = dataclasses.replace(inputs.WORKLOADS["decode32"], name="fused_graph")
+    w = inputs.make_layer(wl, 0, "cuda")
+    d = api.dims_of(wl)
+    wst = api.weights_struct(d, w)
+    xs = [inputs.make_tokens(wl, device="cuda", stream=i) for i in range(2)]
+    wss = [api.workspace(d, wl.T) for _ in range(2)]
+    refs = [api.forward(d, xs[i], w, ws=wss[i], return_routing=True, fused=True) for i in range(2)]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(r) for r in refs[0]]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            api.flint_moe_forward_fused(d, xs[0], wst, *outs, ws=wss[0], stream=s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        api.forward(d, xs[1], w, ws=wss[0], fused=True)  # dirties the workspace
+        for o in outs:
+            o.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs[0]):
+            assert torch.equal(o.view(torch.uint8), ref.view(torch.uint8)), f"replay {r} differs"
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs2 = [[torch.full_like(r, -1) for r in refs[i]] for i in range(2)]
+    for st_ in streams:
+        st_.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for i in (0, 1):
+            api.flint_moe_forward_fused(d, xs[i], wst, *outs2[i], ws=wss[i], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for o, ref in zip(outs2[i], refs[i]):
+            assert torch.equal(o.view(torch.uint8), ref.view(torch.uint8)), f"stream {i} differs"
 
 
 @pytest.mark.parametrize("T", [32, 600])
