@@ -110,6 +110,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     w.h_shared = take((size_t)T * Is * eb);
     w.y_sorted = (float *)take(TK * H * 4);
     w.y_shared = (float *)take((size_t)shared_splits * T * H * 4);
+    if (tiles.tiled && K > 0) w.y_scale = (int8_t *)take(TK * (H / kYScaleCols));
     if (eb == 2 && K > 0 && T <= kFusedMaxT) {  // the fused decode kernel's own state
         w.topk_q = (int32_t *)take((size_t)kFusedQueues * TK * 4);
         w.sync = (int32_t *)take((size_t)kFusedSyncWords * 4);
@@ -349,6 +350,10 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
     a.topk_idx = topk_idx_out ? topk_idx_out : w.topk_idx;
     a.topk_w = topk_w_out ? topk_w_out : w.topk_w;
     a.compute_topk = true;
+    if (!e.mx4 && tiles.tiled) {
+        a.y_scale = w.y_scale;
+        a.scale_cols = d->hidden / kYScaleCols;
+    }
     a.counts = w.counts;
     a.offsets = w.offsets;
     a.sorted_token = w.sorted_token;
@@ -374,6 +379,7 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
     e.h_shared = w.h_shared;
     e.y_sorted = w.y_sorted;
     e.y_shared = w.y_shared;
+    e.y_scale = w.y_scale;
     e.shared_splits = shared_splits;
     e.out = out;
     e.out_bf16 = out_dtype == FLINT_BF16;

@@ -242,6 +242,8 @@ __global__ __launch_bounds__(WaveGrid<SPLIT>::THREADS) void k_down(ExpertArgs a,
 
 // ---------------------------------------------------------------------------
 // out[t] = sum_k w[t][k] * y_sorted[slot_of[t*K+k]] + y_shared[t]   (fixed order)
+// Y16: y_sorted holds fp16 values times 2^y_scale (see ExpertArgs::y16).
+template <bool Y16>
 __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 {
     const int t = blockIdx.x;
@@ -261,9 +263,25 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
             slots[k] = a.slot_of[i];
             w[k] = a.topk_w[i];
         }
+        if (Y16) {
+            typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+            const _Float16 *y16 = reinterpret_cast<const _Float16 *>(a.y_sorted);
+            h16x4 v[kMaxTopK];
+            int8_t sc[kMaxTopK];
 #pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k)
-            y[k] = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
+            for (int k = 0; k < kMaxTopK; ++k) {
+                v[k] = *reinterpret_cast<const h16x4 *>(y16 + (size_t)slots[k] * H + c);
+                sc[k] = a.y_scale[(size_t)slots[k] * (H / kYScaleCols) + c / kYScaleCols];
+            }
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[k][j] = ldexpf((float)v[k][j], sc[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k)
+                y[k] = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
+        }
     }
     const f32x4 ys = a.Is > 0 ? *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -331,17 +349,19 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
 {
     const ExpertTiles &t = a.tiles;
     const Marks m1 = marks ? marks[0] : Marks{}, m2 = marks ? marks[1] : Marks{}, m3 = marks ? marks[2] : Marks{};
-    const dim3 gc(a.T, (a.H + 1023) / 1024);
     if (a.mx4) {
         const hipError_t err = launch_experts_mx4(a, stream, marks);
         if (err != hipSuccess) return err;
-        return a.skip_combine ? hipSuccess : launch_k(k_combine, gc, 256, 0, stream, m3, a);
+        return a.skip_combine ? hipSuccess : launch_combine(a, stream, m3);
     }
     if (t.stream || t.tiled) {
+        // the tiled down product stores the routed rows as scaled fp16
+        ExpertArgs b = a;
+        b.y16 = t.tiled && a.K > 0;
         const hipError_t err =
-            t.stream ? launch_experts_stream(a, stream, marks) : launch_experts_tiled(a, stream, marks);
+            t.stream ? launch_experts_stream(b, stream, marks) : launch_experts_tiled(b, stream, marks);
         if (err != hipSuccess) return err;
-        return a.skip_combine ? hipSuccess : launch_k(k_combine, gc, 256, 0, stream, m3, a);
+        return b.skip_combine ? hipSuccess : launch_combine(b, stream, m3);
     }
     const int cap1 = list_capacity(a.T, a.K, a.E, t.bm1);
     const int cap2 = list_capacity(a.T, a.K, a.E, t.bm2);
@@ -363,13 +383,15 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
     else
         err = launch_k(k_down<DT, 4, 4, 1, 4, false>, g2, 256, 0, stream, m2, a, ns2);
     if (err != hipSuccess) return err;
-    return a.skip_combine ? hipSuccess : launch_k(k_combine, gc, 256, 0, stream, m3, a);
+    return a.skip_combine ? hipSuccess : launch_combine(a, stream, m3);
 }
 
 hipError_t launch_combine(const ExpertArgs &a, hipStream_t stream, Marks m)
 {
     if (a.T <= 0) return hipSuccess;
-    return launch_k(k_combine, dim3(a.T, (a.H + 1023) / 1024), 256, 0, stream, m, a);
+    const dim3 grid(a.T, (a.H + 1023) / 1024);
+    return a.y16 ? launch_k(k_combine<true>, grid, 256, 0, stream, m, a)
+                 : launch_k(k_combine<false>, grid, 256, 0, stream, m, a);
 }
 
 hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks)

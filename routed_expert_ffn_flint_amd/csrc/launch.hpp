@@ -67,6 +67,9 @@ constexpr int kFusedMaxT = 64;
 constexpr int kFusedMaxShared = 8;
 constexpr int kFusedSyncWords = (2 * kFusedQueues + kMaxExperts + kFusedMaxShared + 1) * 32;
 
+// Columns that share one exponent of the fp16 routed outputs (y16).
+constexpr int kYScaleCols = 64;
+
 // Tile shapes of the expert kernels for one launch regime.
 struct ExpertTiles {
     int bm1;  // rows per gate/up tile
@@ -99,8 +102,9 @@ struct Workspace {
     int32_t *meta;        // [4]: list1 length, list2 length
     void *h_sorted;       // [T*K][I] dtype
     void *h_shared;       // [T][Is] dtype
-    float *y_sorted;      // [T*K][H]
+    float *y_sorted;      // [T*K][H] float32, or fp16 (with y_scale) on the tiled kernels
     float *y_shared;      // [T][H]
+    int8_t *y_scale;      // [T*K][H/64]: power-of-two exponents of fp16 y_sorted
     int32_t *topk_q;      // fused decode: [queues][T][K] per-queue copies of the selection
     int32_t *sync;        // fused decode: kFusedSyncWords counters
     size_t bytes;         // total bytes needed
@@ -147,6 +151,10 @@ struct DispatchArgs {
     int32_t *counts, *offsets, *sorted_token, *slot_of;
     int32_t *list1, *list2, *meta;
     int bm1, bm2;
+    // the exponents of the tiled down product's fp16 outputs, cleared by the
+    // dispatch's scatter kernel ([T*K][scale_cols] bytes; null: none)
+    int8_t *y_scale;
+    int scale_cols;
 };
 hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks m = {});
 
@@ -163,6 +171,11 @@ struct ExpertArgs {
     const int32_t *list1, *list2, *meta;
     void *h_sorted, *h_shared;
     float *y_sorted, *y_shared;
+    // The tiled down product stores routed rows of y_sorted as fp16 times
+    // 2^y_scale[slot][c / 64] (an exponent per row and 64 columns, 0 unless
+    // the row's 64 values reach 2^15); the combine reads them back.
+    bool y16;
+    int8_t *y_scale;
     // The shared expert's down product split over its reduction into this many
     // partial arrays y_shared[s] (the streaming kernels only; 1 elsewhere), which
     // the combine adds in order: a dense layer at decode sizes has too few

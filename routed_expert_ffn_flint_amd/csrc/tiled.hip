@@ -154,6 +154,21 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 
 enum Mode { GATE_UP = 0, DOWN = 1, ROUTER = 2 };
 
+// The largest of v over each row of 16 lanes (lanes 16k .. 16k+15), in every
+// lane of the row: DPP swaps within quads, then the mirrors of 8 and of 16
+// lanes (VALU operations, no LDS traffic).
+__device__ __forceinline__ float row16_max(float v)
+{
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+    return v;
+}
+
 }  // namespace
 
 struct TiledArgs {
@@ -433,12 +448,58 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
     wait_lds();
 
     // ---- epilogue: lane holds C[(lane>>4)*4 + i][lane&15] of each 16x16 block
+    // Routed down rows are stored as fp16 times 2^s, one exponent s per row
+    // and 64 columns (four 16-column blocks): s = 0 unless the 64 values'
+    // largest magnitude reaches 2^15, then the smallest s that brings it
+    // below (so no finite value overflows fp16); the combine multiplies back.
+    // The exponents start at 0 (the dispatch clears them); a wave none of
+    // whose values reaches 2^15 -- the usual case -- stores none.
+    // With 64-column wave tiles the fp16 rows are first gathered in the
+    // (by now idle) LDS stages, one wave-tile region per wave, and then
+    // written out as 16-byte pieces of whole rows instead of 2-byte scattered
+    // stores.
+    constexpr int kGroups = (MODE == DOWN) ? NB / 4 : 1;
+    static_assert(MODE != DOWN || NB % 4 == 0, "64-column exponent groups");
+    const bool y16 = MODE == DOWN && !shared && a.y16;
+    constexpr bool kStaged = MODE == DOWN && C::WN == 64;
+    constexpr int kWavesPerStage = C::STAGE_ELEMS / (C::WM * C::WN);
+    static_assert(!kStaged || C::WAVES <= STAGES * kWavesPerStage, "a wave-tile region of LDS per wave");
+    _Float16 *ystage = nullptr;
+    bool scaled = false;  // some value of this wave reaches 2^15 (uniform over the wave)
+    if (MODE == DOWN && y16) {
+        float mx = 0.f;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[m][j][i]));
+        scaled = __ballot(!(mx < 32768.0f)) != 0;  // (NaN counts as large: it takes the careful path)
+    }
+    if (kStaged && y16) {
+        __syncthreads();  // every wave is done with the stages
+        ystage = reinterpret_cast<_Float16 *>(stage(wave / kWavesPerStage)) + (wave % kWavesPerStage) * C::WM * C::WN;
+    }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = wm * C::WM + m * 16 + (lane >> 4) * 4 + i;
             const int r = row0 + rl;
+            int sexp[kGroups];
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) sexp[g] = 0;
+            if (MODE == DOWN && y16 && scaled) {
+#pragma unroll
+                for (int g = 0; g < kGroups; ++g) {
+                    float mx = 0.f;
+#pragma unroll
+                    for (int j = 4 * g; j < 4 * g + 4; ++j) mx = fmaxf(mx, fabsf(acc[m][j][i]));
+                    mx = row16_max(mx);  // the row's 16 lanes
+                    const int e = (int)((__float_as_uint(mx) >> 23) & 255u) - 126;  // mx < 2^e
+                    sexp[g] = (mx >= 32768.0f && e <= 128) ? e - 15 : 0;
+                }
+            }
             if (r >= row_end) continue;
             if (MODE == GATE_UP) {
                 S *hout = shared ? (S *)a.h_shared : (S *)a.h_sorted;
@@ -449,10 +510,37 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
                     hout[(size_t)r * width + ch] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + NB / 2][i]));
                 }
             } else if (MODE == DOWN) {
+                if (y16) {
+                    if (kStaged) {
+                        // row rl of the wave tile, 16-byte chunk j*2 + (lane&15)/8 stored at
+                        // chunk ^ (row & 7)
+                        const int rw = m * 16 + (lane >> 4) * 4 + i;
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const int c = nt * BN + wn * C::WN + j * 16 + (lane & 15);
-                    if (c < H) yout[(size_t)r * H + c] = acc[m][j][i];
+                        for (int j = 0; j < NB; ++j) {
+                            const int col = j * 16 + (lane & 15);
+                            const int pc = (col >> 3) ^ (rw & 7);
+                            ystage[rw * 64 + pc * 8 + (col & 7)] = (_Float16)ldexpf(acc[m][j][i], -sexp[j / 4]);
+                        }
+                    } else {
+                        _Float16 *y = reinterpret_cast<_Float16 *>(yout);
+#pragma unroll
+                        for (int j = 0; j < NB; ++j) {
+                            const int c = nt * BN + wn * C::WN + j * 16 + (lane & 15);
+                            if (c < H) y[(size_t)r * H + c] = (_Float16)ldexpf(acc[m][j][i], -sexp[j / 4]);
+                        }
+                    }
+#pragma unroll
+                    for (int g = 0; g < kGroups; ++g) {
+                        const int c = nt * BN + wn * C::WN + g * 64;
+                        if (scaled && (lane & 15) == 0 && c < H)
+                            a.y_scale[(size_t)r * (H / kYScaleCols) + c / kYScaleCols] = (int8_t)sexp[g];
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const int c = nt * BN + wn * C::WN + j * 16 + (lane & 15);
+                        if (c < H) yout[(size_t)r * H + c] = acc[m][j][i];
+                    }
                 }
             } else {
 #pragma unroll
@@ -461,6 +549,19 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
                     if (c < a.E) lout[(size_t)r * a.E + c] = acc[m][j][i] + (ta.bias ? ta.bias[c] : 0.f);
                 }
             }
+        }
+    }
+    if (kStaged && y16) {
+        // whole rows out: 8 lanes a row (16 bytes each), 8 rows an instruction
+        typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+        const int c = nt * BN + wn * C::WN;
+        _Float16 *y = reinterpret_cast<_Float16 *>(yout);
+#pragma unroll
+        for (int p = 0; p < C::WM / 8; ++p) {
+            const int rw = p * 8 + lane / 8, c8 = lane % 8;
+            const u32x4v v = *reinterpret_cast<const u32x4v *>(ystage + rw * 64 + (c8 ^ (rw & 7)) * 8);
+            const int r = row0 + wm * C::WM + rw;
+            if (r < row_end && c < H) *reinterpret_cast<u32x4v *>(y + (size_t)r * H + c + c8 * 8) = v;
         }
     }
 }
