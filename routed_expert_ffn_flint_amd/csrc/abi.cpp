@@ -125,9 +125,7 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
 // every down item of the persistent walk is the same length.  Measured (Flint
 // shape): T = 32 down 57.6 -> 55.5 us, T = 8 23.0 -> 22.3 us; at T = 128 the
 // extra partial array costs more than the balance gains, at 256 it is even.
-#ifndef FLINT_MOE_SHARED_SPLIT_T
-#define FLINT_MOE_SHARED_SPLIT_T 64
-#endif
+constexpr int kMoeSharedSplitT = 64;
 static bool fused_ok(const flint_moe_dims *d, int32_t T)
 {
     return fused_eligible(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter, d->dtype == FLINT_BF16);
@@ -138,7 +136,7 @@ static bool fused_ok(const flint_moe_dims *d, int32_t T)
 int moe_shared_splits(const flint_moe_dims *d, int32_t T, bool mx4, bool fused = false)
 {
     if (fused) return d->shared_inter > 0 ? d->shared_inter / d->inter : 1;
-    if (T > FLINT_MOE_SHARED_SPLIT_T || mx4 || d->shared_inter <= d->inter || d->shared_inter % d->inter) return 1;
+    if (T > kMoeSharedSplitT || mx4 || d->shared_inter <= d->inter || d->shared_inter % d->inter) return 1;
     const int s = d->shared_inter / d->inter;
     if (s > 8) return 1;
     const bool bf16 = d->dtype == FLINT_BF16;

@@ -24,30 +24,14 @@ namespace flint {
 // Small-batch tile shapes (decode): rows per tile 32 (MB = 2 blocks of 16),
 // split-k over SPLIT waves.  Gate/up: NB/2 channels-blocks of 16 per tile;
 // down: NB column blocks of 16 per tile.
-#ifndef FLINT_GU_NB
-#define FLINT_GU_NB 4
-#endif
-#ifndef FLINT_GU_SPLIT
-#define FLINT_GU_SPLIT 4
-#endif
-#ifndef FLINT_GU_UNROLL
-#define FLINT_GU_UNROLL 4
-#endif
-#ifndef FLINT_DN_NB
-#define FLINT_DN_NB 4
-#endif
-#ifndef FLINT_DN_SPLIT
-#define FLINT_DN_SPLIT 4
-#endif
-#ifndef FLINT_DN_UNROLL
-#define FLINT_DN_UNROLL 4
-#endif
-#ifndef FLINT_GU_PIPE
-#define FLINT_GU_PIPE false
-#endif
-#ifndef FLINT_DN_PIPE
-#define FLINT_DN_PIPE false
-#endif
+constexpr int kGuNb = 4;
+constexpr int kGuSplit = 4;
+constexpr int kGuUnroll = 4;
+constexpr int kDnNb = 4;
+constexpr int kDnSplit = 4;
+constexpr int kDnUnroll = 4;
+constexpr bool kGuPipe = false;
+constexpr bool kDnPipe = false;
 
 template <int SPLIT> struct WaveGrid {  // SPLIT waves, same tile, k split SPLIT ways
     static constexpr int WM = 1, WN = 1, THREADS = SPLIT * 64;
@@ -325,20 +309,16 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 }
 
 // ---------------------------------------------------------------------------
-#ifndef FLINT_USE_STREAM
-#define FLINT_USE_STREAM 1
-#endif
-
 ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf16)
 {
     const bool tiled = tiled_eligible(T, K, E, H, I, Is, bf16);
     const int small_max = tiled ? (K > 0 ? kTiledFromT : kDenseTiledFromT) - 1 : kStreamMaxT;
     if (T <= small_max) {
-        if (FLINT_USE_STREAM && stream_eligible(T, H, I, Is))
+        if (stream_eligible(T, H, I, Is))
             return ExpertTiles{stream_bm1(T, K), 0, stream_bm2(), 0, true, true, false};
         // Small batches (decode): split-k kernels over 32-row tiles, so that one
         // tile holds every row an expert gets and each weight is read once.
-        return ExpertTiles{32, FLINT_GU_NB / 2 * 16, 32, FLINT_DN_NB * 16, true, false, false};
+        return ExpertTiles{32, kGuNb / 2 * 16, 32, kDnNb * 16, true, false, false};
     }
     if (tiled) return ExpertTiles{tiled_bm1(T, K, E, Is), 0, tiled_bm2(T, K, E), 0, false, false, true};
     return ExpertTiles{128, 64, 128, 128, false, false, false};
@@ -372,14 +352,14 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
     const int g2 = ns2 + cap2 * ((a.H + t.bn2 - 1) / t.bn2);
     hipError_t err;
     if (t.small)
-        err = launch_k(k_gate_up<DT, 2, FLINT_GU_NB, FLINT_GU_SPLIT, FLINT_GU_UNROLL, FLINT_GU_PIPE>, g1,
-                       WaveGrid<FLINT_GU_SPLIT>::THREADS, 0, stream, m1, a, ns1);
+        err = launch_k(k_gate_up<DT, 2, kGuNb, kGuSplit, kGuUnroll, kGuPipe>, g1,
+                       WaveGrid<kGuSplit>::THREADS, 0, stream, m1, a, ns1);
     else
         err = launch_k(k_gate_up<DT, 4, 4, 1, 4, false>, g1, 256, 0, stream, m1, a, ns1);
     if (err != hipSuccess) return err;
     if (t.small)
-        err = launch_k(k_down<DT, 2, FLINT_DN_NB, FLINT_DN_SPLIT, FLINT_DN_UNROLL, FLINT_DN_PIPE>, g2,
-                       WaveGrid<FLINT_DN_SPLIT>::THREADS, 0, stream, m2, a, ns2);
+        err = launch_k(k_down<DT, 2, kDnNb, kDnSplit, kDnUnroll, kDnPipe>, g2,
+                       WaveGrid<kDnSplit>::THREADS, 0, stream, m2, a, ns2);
     else
         err = launch_k(k_down<DT, 4, 4, 1, 4, false>, g2, 256, 0, stream, m2, a, ns2);
     if (err != hipSuccess) return err;

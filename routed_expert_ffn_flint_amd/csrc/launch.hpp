@@ -51,14 +51,8 @@ constexpr int kStreamMaxT = 512;
 // from 385 rows for a MoE layer (Flint shape: T = 512 401 -> 385 us; even at
 // 384), from 129 rows for a dense layer, whose weights the streaming kernels
 // read again for every 32 rows (T = 192: 108 -> 74 us; even at 128).
-#ifndef FLINT_TILED_FROM_T
-#define FLINT_TILED_FROM_T 385
-#endif
-#ifndef FLINT_DENSE_TILED_FROM_T
-#define FLINT_DENSE_TILED_FROM_T 129
-#endif
-constexpr int kTiledFromT = FLINT_TILED_FROM_T;
-constexpr int kDenseTiledFromT = FLINT_DENSE_TILED_FROM_T;
+constexpr int kTiledFromT = 385;
+constexpr int kDenseTiledFromT = 129;
 
 // The persistent fused decode kernel (fused.hip): queues (work-group classes),
 // largest batch, most shared-expert slices, and its counter words.
@@ -219,10 +213,7 @@ hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const M
 int tiled_dense_splits(int T, int H, int Is);
 // The router product on the same tiles (large bf16 batches).
 bool tiled_router_eligible(int T, int H, bool bf16);
-#ifndef FLINT_ROUTER_SPLITS
-#define FLINT_ROUTER_SPLITS 4
-#endif
-constexpr int kRouterSplits = FLINT_ROUTER_SPLITS;
+constexpr int kRouterSplits = 4;
 hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, const float *bias, int E,
                                float *logits, hipStream_t stream, Marks m);
 

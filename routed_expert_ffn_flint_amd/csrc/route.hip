@@ -27,18 +27,11 @@
 //   k_dispatch_scatter (more than one tile) slot = offset + tile base + rank.
 #include <climits>
 
-#ifndef FLINT_TOPK_WAVE_T
-#define FLINT_TOPK_WAVE_T 4096  // largest batch selected one token per wave (16 lanes per token above)
-#endif
-#ifndef FLINT_TOPK_FUSED_T
+constexpr int kTopkWaveT = 4096;  // largest batch selected one token per wave (16 lanes per token above)
 // Largest batch whose top-k and dispatch run as one work-group of 16 waves,
 // one token per wave (T = 8: 10.2 -> 7.4 us; with two tokens per wave their
 // latencies add up: T = 32 9.8 -> 12.9 us).
-#define FLINT_TOPK_FUSED_T 16
-#endif
-#ifndef FLINT_TOPK_WAVE
-#define FLINT_TOPK_WAVE 1  // up to FLINT_TOPK_WAVE_T: bitwise K-th-largest search (1) or sorted-list merges (0)
-#endif
+constexpr int kTopkFusedT = 16;
 
 #include "gemm_core.hpp"
 #include "launch.hpp"
@@ -130,16 +123,14 @@ __global__ __launch_bounds__(SPLIT > 1 ? SPLIT * 64 : 256) void k_router_logits(
 // its own partial array (top-k adds the two in order), so twice as many CUs
 // read the router matrix: measured 5.8 -> 4.2 us at T = 32 (four or eight
 // partial arrays cost top-k more than they save).
-#ifndef FLINT_ROUTER_SMALL_SPLITS
-#define FLINT_ROUTER_SMALL_SPLITS 2
-#endif
-static_assert(FLINT_ROUTER_SMALL_SPLITS == 1 || FLINT_ROUTER_SMALL_SPLITS == 2 || FLINT_ROUTER_SMALL_SPLITS == 4 ||
-                  FLINT_ROUTER_SMALL_SPLITS == 8,
+constexpr int kRouterSmallSplits = 2;
+static_assert(kRouterSmallSplits == 1 || kRouterSmallSplits == 2 || kRouterSmallSplits == 4 ||
+                  kRouterSmallSplits == 8,
               "router splits: 1, 2, 4 or 8 (16 / splits waves per work-group)");
 int small_router_splits(int T, int H, int E)
 {
     const long long tiles = (long long)((E + 15) / 16) * ((T + 15) / 16);
-    const int s = FLINT_ROUTER_SMALL_SPLITS;
+    const int s = kRouterSmallSplits;
     return s > 1 && tiles < 128 && H % (32 * s) == 0 ? s : 1;
 }
 
@@ -567,10 +558,10 @@ hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks
     // the first kernel carries m.start, the last m.stop
     Marks first{m.start, a.dispatch ? nullptr : m.stop};
     hipError_t err = hipSuccess;
-    if (a.compute_topk && a.dispatch && fused && a.T <= FLINT_TOPK_FUSED_T && FLINT_TOPK_WAVE && a.E <= 256)
+    if (a.compute_topk && a.dispatch && fused && a.T <= kTopkFusedT && a.E <= 256)
         return launch_k(k_topk_dispatch_small, 1, 1024, 0, stream, m, a);
     if (a.compute_topk) {
-        err = a.T <= FLINT_TOPK_WAVE_T ? launch_k(FLINT_TOPK_WAVE ? k_topk_wave : k_topk<64>, (a.T + 3) / 4, 256, 0, stream, first, a)
+        err = a.T <= kTopkWaveT ? launch_k(k_topk_wave, (a.T + 3) / 4, 256, 0, stream, first, a)
                           : launch_k(k_topk<16>, (a.T + 15) / 16, 256, 0, stream, first, a);
         if (err != hipSuccess) return err;
         first.start = nullptr;

@@ -25,45 +25,23 @@
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
-#ifndef FLINT_ST_NB1
-#define FLINT_ST_NB1 4  // gate/up items: NB1/2 blocks of 16 channels
-#endif
-#ifndef FLINT_ST_NB2
-#define FLINT_ST_NB2 2  // down items: NB2 blocks of 16 columns
-#endif
-#ifndef FLINT_ST_UMAX1
-#define FLINT_ST_UMAX1 2  // gate/up slices per batch (register budget: 2 batches in flight)
-#endif
-#ifndef FLINT_ST_UMAX2
-#define FLINT_ST_UMAX2 2  // down slices per batch
-#endif
-#ifndef FLINT_ST_MB1
-#define FLINT_ST_MB1 2  // gate/up items: MB1 blocks of 16 rows
-#endif
-// Batches of at most FLINT_ST_SMALL_T tokens (an expert then gets a row or
-// two) use gate/up items of FLINT_ST_MB1S row blocks x FLINT_ST_NB1S column
+constexpr int kStNb1 = 4;  // gate/up items: NB1/2 blocks of 16 channels
+constexpr int kStNb2 = 2;  // down items: NB2 blocks of 16 columns
+constexpr int kStUmax1 = 2;  // gate/up slices per batch (register budget: 2 batches in flight)
+constexpr int kStUmax2 = 2;  // down slices per batch
+constexpr int kStMb1 = 2;  // gate/up items: MB1 blocks of 16 rows
+// Batches of at most kStSmallT tokens (an expert then gets a row or
+// two) use gate/up items of kStMb1s row blocks x kStNb1s column
 // blocks: half the activation loads, and twice the items, which evens out the
 // last round of the persistent grid (measured 108 -> 103 us at T = 32; at
 // T = 256 the larger items are faster).
-#ifndef FLINT_ST_SMALL_T
-#define FLINT_ST_SMALL_T 64
-#endif
-#ifndef FLINT_ST_MB1S
-#define FLINT_ST_MB1S 1
-#endif
-#ifndef FLINT_ST_NB1S
-#define FLINT_ST_NB1S 2
-#endif
-#ifndef FLINT_ST_WGS1
-#define FLINT_ST_WGS1 2  // gate/up: work-groups per CU (the grid; also the occupancy asked for)
-#endif
-#ifndef FLINT_ST_WGS2
-#define FLINT_ST_WGS2 2  // down
-#endif
+constexpr int kStSmallT = 64;
+constexpr int kStMb1s = 1;
+constexpr int kStNb1s = 2;
+constexpr int kStWgs1 = 2;  // gate/up: work-groups per CU (the grid; also the occupancy asked for)
+constexpr int kStWgs2 = 2;  // down
 
-#ifndef FLINT_ST_MB2
-#define FLINT_ST_MB2 2  // down items: MB2 blocks of 16 rows
-#endif
+constexpr int kStMb2 = 2;  // down items: MB2 blocks of 16 rows
 
 namespace flint {
 
@@ -108,7 +86,7 @@ struct Item {
 
 // GATE_UP: gate/up + SwiGLU -> h (dtype);  otherwise: down -> y (float32).
 template <typename DT, int MB, int NB, int U, bool GATE_UP>
-__global__ __launch_bounds__(256, GATE_UP ? FLINT_ST_WGS1 : FLINT_ST_WGS2) void k_expert_stream(ExpertArgs a,
+__global__ __launch_bounds__(256, GATE_UP ? kStWgs1 : kStWgs2) void k_expert_stream(ExpertArgs a,
                                                                                           int n_shared_items)
 {
     using S = typename DT::storage;
@@ -298,11 +276,11 @@ static int unroll_for(const int *dims, int n, int umax)
     }
     return 0;
 }
-static int unroll_gate_up(int H) { return unroll_for(&H, 1, FLINT_ST_UMAX1); }
+static int unroll_gate_up(int H) { return unroll_for(&H, 1, kStUmax1); }
 static int unroll_down(int I, int Is)
 {
     const int d[2] = {I, Is > 0 ? Is : I};
-    return unroll_for(d, 2, FLINT_ST_UMAX2);
+    return unroll_for(d, 2, kStUmax2);
 }
 
 bool stream_eligible(int T, int H, int I, int Is)
@@ -311,20 +289,20 @@ bool stream_eligible(int T, int H, int I, int Is)
 }
 // (routed layers only: a dense layer's gate/up items are all shared-expert
 // items, and there the 32 x 64 items measured faster at T = 32, 18 vs 22 us)
-static bool small_batch(int T, int K) { return T <= FLINT_ST_SMALL_T && K > 0; }
-int stream_bm1(int T, int K) { return (small_batch(T, K) ? FLINT_ST_MB1S : FLINT_ST_MB1) * 16; }
-int stream_bm2() { return FLINT_ST_MB2 * 16; }
+static bool small_batch(int T, int K) { return T <= kStSmallT && K > 0; }
+int stream_bm1(int T, int K) { return (small_batch(T, K) ? kStMb1s : kStMb1) * 16; }
+int stream_bm2() { return kStMb2 * 16; }
 
 template <typename DT, int U, bool GATE_UP>
 static hipError_t launch_one(const ExpertArgs &a, int grid, int n_shared, size_t lds, hipStream_t stream, Marks m)
 {
     if (GATE_UP && small_batch(a.T, a.K))
-        return launch_k(k_expert_stream<DT, FLINT_ST_MB1S, FLINT_ST_NB1S, U, true>, grid, 256, lds, stream, m, a,
+        return launch_k(k_expert_stream<DT, kStMb1s, kStNb1s, U, true>, grid, 256, lds, stream, m, a,
                         n_shared);
     if (GATE_UP)
-        return launch_k(k_expert_stream<DT, FLINT_ST_MB1, FLINT_ST_NB1, U, true>, grid, 256, lds, stream, m, a,
+        return launch_k(k_expert_stream<DT, kStMb1, kStNb1, U, true>, grid, 256, lds, stream, m, a,
                         n_shared);
-    return launch_k(k_expert_stream<DT, FLINT_ST_MB2, FLINT_ST_NB2, U, false>, grid, 256, lds, stream, m, a, n_shared);
+    return launch_k(k_expert_stream<DT, kStMb2, kStNb2, U, false>, grid, 256, lds, stream, m, a, n_shared);
 }
 
 template <typename DT, bool GATE_UP>
@@ -339,8 +317,8 @@ static hipError_t launch_u(int U, const ExpertArgs &a, int grid, int n_shared, s
 template <typename DT>
 static hipError_t launch_stream_t(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
-    const int bm1 = stream_bm1(a.T, a.K), bm2 = FLINT_ST_MB2 * 16;
-    const int bn1 = (small_batch(a.T, a.K) ? FLINT_ST_NB1S : FLINT_ST_NB1) / 2 * 16, bn2 = FLINT_ST_NB2 * 16;
+    const int bm1 = stream_bm1(a.T, a.K), bm2 = kStMb2 * 16;
+    const int bn1 = (small_batch(a.T, a.K) ? kStNb1s : kStNb1) / 2 * 16, bn2 = kStNb2 * 16;
     const int cap1 = list_capacity(a.T, a.K, a.E, bm1);
     const int cap2 = list_capacity(a.T, a.K, a.E, bm2);
     const int ns1 = a.Is > 0 ? (a.T + bm1 - 1) / bm1 * (a.Is / bn1) : 0;
@@ -350,10 +328,10 @@ static hipError_t launch_stream_t(const ExpertArgs &a, hipStream_t stream, const
     const int max2 = ns2 + cap2 * ((a.H + bn2 - 1) / bn2);
     const size_t lds1 = (size_t)(2 * cap1 + a.E + 1) * 4;
     const size_t lds2 = (size_t)(2 * cap2 + a.E + 1) * 4;
-    const hipError_t err = launch_u<DT, true>(unroll_gate_up(a.H), a, min(FLINT_ST_WGS1 * a.cus, max1), ns1, lds1, stream,
+    const hipError_t err = launch_u<DT, true>(unroll_gate_up(a.H), a, min(kStWgs1 * a.cus, max1), ns1, lds1, stream,
                                               marks ? marks[0] : Marks{});
     if (err != hipSuccess) return err;
-    return launch_u<DT, false>(unroll_down(a.I, a.Is / nsplit), a, min(FLINT_ST_WGS2 * a.cus, max2), ns2, lds2, stream,
+    return launch_u<DT, false>(unroll_down(a.I, a.Is / nsplit), a, min(kStWgs2 * a.cus, max2), ns2, lds2, stream,
                                marks ? marks[1] : Marks{});
 }
 

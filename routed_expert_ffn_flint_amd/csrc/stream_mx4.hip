@@ -35,42 +35,7 @@
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
-#ifndef FLINT_MX_MB1
-#define FLINT_MX_MB1 1  // gate/up items: MB1 blocks of 16 rows
-#endif
-#ifndef FLINT_MX_MB2
-#define FLINT_MX_MB2 1  // down items
-#endif
-#ifndef FLINT_MX_NB1
-#define FLINT_MX_NB1 4  // gate/up items: NB1/2 blocks of 16 channels (gate and up each)
-#endif
-#ifndef FLINT_MX_NB2
-#define FLINT_MX_NB2 4  // down items: NB2 blocks of 16 output columns
-#endif
-#ifndef FLINT_MX_CK1
-#define FLINT_MX_CK1 128  // gate/up: k per wave and step
-#endif
-#ifndef FLINT_MX_CK2
-#define FLINT_MX_CK2 128  // down
-#endif
-#ifndef FLINT_MX_KS1
-#define FLINT_MX_KS1 4  // gate/up: waves sharing an item (4: split reduction; 1: a wave per item)
-#endif
-#ifndef FLINT_MX_KS2
-#define FLINT_MX_KS2 1  // down
-#endif
-#ifndef FLINT_MX_WIDE1_T
-#define FLINT_MX_WIDE1_T 256  // gate/up items of 2 * NB1 column blocks from this batch size on
-#endif
-#ifndef FLINT_MX_WIDE2_T
-#define FLINT_MX_WIDE2_T 128  // down items of 2 * NB2 column blocks from this batch size on
-#endif
-#ifndef FLINT_MX_GRID_ALL
-#define FLINT_MX_GRID_ALL 0  // one work-group per item instead of a persistent grid
-#endif
-#ifndef FLINT_MX_WGS
-#define FLINT_MX_WGS 2  // work-groups per CU (grid and occupancy)
-#endif
+constexpr int kMxWgs = 2;  // work-groups per CU (grid and occupancy)
 
 namespace flint {
 
@@ -138,7 +103,7 @@ struct MxItem {
 // reduction each, and add their partial sums in LDS; KSPLIT 1: every wave
 // walks its own items over the whole reduction (no LDS sums, no barriers).
 template <int MB, int NB, int CK, bool GATE_UP, int KSPLIT>
-__global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertArgs a, int n_shared_items)
+__global__ __launch_bounds__(256, kMxWgs) void k_expert_stream_mx4(ExpertArgs a, int n_shared_items)
 {
     constexpr int BM = MB * 16;
     constexpr int HALF = NB / 2;
@@ -337,14 +302,18 @@ __global__ __launch_bounds__(256, FLINT_MX_WGS) void k_expert_stream_mx4(ExpertA
 }
 
 namespace {
-constexpr int kMxMB1 = FLINT_MX_MB1, kMxMB2 = FLINT_MX_MB2;
-constexpr int kMxNB1 = FLINT_MX_NB1, kMxNB2 = FLINT_MX_NB2;
-constexpr int kMxCK1 = FLINT_MX_CK1, kMxCK2 = FLINT_MX_CK2;
-constexpr int kMxKS1 = FLINT_MX_KS1, kMxKS2 = FLINT_MX_KS2;
+// gate/up (1) and down (2) items: MB blocks of 16 rows; NB blocks of 16
+// columns (gate/up: NB/2 blocks of gate and of up channels); CK of the
+// reduction per wave and step; KS waves sharing an item (KS 4: split
+// reduction; 1: a wave per item)
+constexpr int kMxMB1 = 1, kMxMB2 = 1;
+constexpr int kMxNB1 = 4, kMxNB2 = 4;
+constexpr int kMxCK1 = 128, kMxCK2 = 128;
+constexpr int kMxKS1 = 4, kMxKS2 = 1;
 // From these batch sizes on, items twice as wide (an expert then has enough
 // rows that fewer, larger items pay: measured at T = 512 gate/up 86 -> 77 us,
 // down 45 -> 41 us; at T <= 128 the narrow gate/up items are faster)
-constexpr int kMxWide1T = FLINT_MX_WIDE1_T, kMxWide2T = FLINT_MX_WIDE2_T;
+constexpr int kMxWide1T = 256, kMxWide2T = 128;
 
 int nb1_for(int T) { return T >= kMxWide1T ? 2 * kMxNB1 : kMxNB1; }
 int nb2_for(int T) { return T >= kMxWide2T ? 2 * kMxNB2 : kMxNB2; }
@@ -359,7 +328,7 @@ hipError_t launch_mx4_nb(const ExpertArgs &a, hipStream_t stream, const Marks *m
     const int ns2 = a.Is > 0 ? (a.T + bm2 - 1) / bm2 * (a.H / bn2) : 0;
     const int max1 = ns1 + cap1 * (a.I / bn1);
     const int max2 = ns2 + cap2 * (a.H / bn2);
-    const int grid_cap = FLINT_MX_GRID_ALL ? (1 << 30) : FLINT_MX_WGS * max(a.cus, 1);
+    const int grid_cap = kMxWgs * max(a.cus, 1);
     // work-groups to cover every item once: an item per work-group (KSPLIT 4) or per wave (1)
     const int g1 = kMxKS1 > 1 ? max1 : (max1 + kWavesMx - 1) / kWavesMx;
     const int g2 = kMxKS2 > 1 ? max2 : (max2 + kWavesMx - 1) / kWavesMx;

@@ -52,10 +52,7 @@ namespace flint {
 namespace {
 
 constexpr int kXcds = 8;
-#ifndef FLINT_TL_GROUP
-#define FLINT_TL_GROUP 8
-#endif
-constexpr int kRowGroup = FLINT_TL_GROUP;  // row tiles per group of shared-weight items
+constexpr int kRowGroup = 8;  // row tiles per group of shared-weight items
 constexpr int kLdsBytes = 160 * 1024;
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
@@ -85,32 +82,13 @@ struct Cfg {
 };
 
 // Configurations (chosen per launch by the host).
-#ifndef FLINT_TL_ROTATE
-#define FLINT_TL_ROTATE 1
-#endif
-#ifndef FLINT_TL_SKIP_DEAD
-#define FLINT_TL_SKIP_DEAD 1
-#endif
-#ifndef FLINT_TL_S_BK
-#define FLINT_TL_S_BK 32
-#endif
-#ifndef FLINT_TL_S_ST
-#define FLINT_TL_S_ST 5
-#endif
-#ifndef FLINT_TL_N_ST
-#define FLINT_TL_N_ST 3
-#endif
-#ifndef FLINT_TL_B_ST
-#define FLINT_TL_B_ST 4
-#endif
-using CfgSmall = Cfg<128, 128, 64, 64, FLINT_TL_S_BK, FLINT_TL_S_ST>;  // 4 waves
-using CfgWide = Cfg<256, 128, 128, 64, 32, 6>;                         // 4 waves
-using CfgBig = Cfg<256, 256, 128, 128, 32, FLINT_TL_B_ST>;             // 4 waves
-using CfgBig8 = Cfg<256, 256, 128, 64, 32, FLINT_TL_B_ST>;             // 8 waves
-#ifndef FLINT_TL_N_BK
-#define FLINT_TL_N_BK 64  // 128 x 256 tiles: 64-wide slices in 3 stages (T = 4096: 570 -> 560 us vs 32 x 4)
-#endif
-using CfgWideN = Cfg<128, 256, 64, 64, FLINT_TL_N_BK, FLINT_TL_N_ST>;   // 8 waves
+// Cfg<BM, BN, WM, WN, BK, STAGES>; the 128 x 256 tiles take 64-wide slices
+// in 3 stages (T = 4096: 570 -> 560 us against 32-wide slices in 4).
+using CfgSmall = Cfg<128, 128, 64, 64, 32, 5>;  // 4 waves
+using CfgWide = Cfg<256, 128, 128, 64, 32, 6>;  // 4 waves
+using CfgBig = Cfg<256, 256, 128, 128, 32, 4>;  // 4 waves
+using CfgBig8 = Cfg<256, 256, 128, 64, 32, 4>;  // 8 waves
+using CfgWideN = Cfg<128, 256, 64, 64, 64, 3>;  // 8 waves
 
 // Item of this work-group, or -1 (see the file comment).  Work-groups are
 // dealt to the XCDs round-robin (blockIdx.x % 8 is the XCD); the grid is sized
@@ -379,7 +357,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
     // 1 KB rows (measured faster).  Gate/up products keep one order: there the
     // n-tiles of an expert tile read the same gathered rows at the same time,
     // from L2.
-    const int rot = (MODE == DOWN && FLINT_TL_ROTATE) ? (int)(blockIdx.x * 7u % (unsigned)nk) : 0;
+    const int rot = MODE == DOWN ? (int)(blockIdx.x * 7u % (unsigned)nk) : 0;
     auto kofs = [&](int s) {
         s = min(s, nk - 1) + rot;
         return (s >= nk ? s - nk : s) * BK;
@@ -435,14 +413,12 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
             for (int q = 0; q < C::NQ; ++q) step(live, j, q, nfull + j);
         }
     };
-#if FLINT_TL_SKIP_DEAD
+    // waves whose rows all lie past the tile's end skip the MFMAs (they still
+    // take part in the loads and barriers)
     if (row0 + wm * C::WM < row_end)
         run(std::integral_constant<bool, true>{});
     else
         run(std::integral_constant<bool, false>{});
-#else
-    run(std::integral_constant<bool, true>{});
-#endif
     // no load may still be writing this work-group's LDS when it exits
     wait_vmcnt<0>();
     wait_lds();
@@ -569,24 +545,11 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
 // ---------------------------------------------------------------------------
 // Host side
 
-#ifndef FLINT_TL_BIG_ROWS
-#define FLINT_TL_BIG_ROWS 256  // mean rows per expert from which the big configurations are used
-#endif
-#ifndef FLINT_TL_GU_SMALL
-#define FLINT_TL_GU_SMALL 6  // gate/up below that: 0 CfgSmall, 1 CfgWide, 6 CfgWideN (T = 4096: 290 -> 280 us)
-#endif
-#ifndef FLINT_TL_GU_BIG
-#define FLINT_TL_GU_BIG 3  // gate/up from there: 2 CfgBig, 3 CfgBig8 (or 0, 1)
-#endif
-#ifndef FLINT_TL_DN_SMALL
-#define FLINT_TL_DN_SMALL 6  // (T = 2048: 128 x 256 tiles 154 -> 144 us; even at 4096)
-#endif
-#ifndef FLINT_TL_DN_BIG
-#define FLINT_TL_DN_BIG 3  // (T = 16384: 8 waves measured 3% faster for the layer than 4)
-#endif
-#ifndef FLINT_TL_ROUTER
-#define FLINT_TL_ROUTER 0
-#endif
+constexpr int kTlBigRows = 256;  // mean rows per expert from which the big configurations are used
+constexpr int kTlGuSmall = 6;  // gate/up below that: 0 CfgSmall, 1 CfgWide, 6 CfgWideN (T = 4096: 290 -> 280 us)
+constexpr int kTlGuBig = 3;  // gate/up from there: 2 CfgBig, 3 CfgBig8 (or 0, 1)
+constexpr int kTlDnSmall = 6;  // (T = 2048: 128 x 256 tiles 154 -> 144 us; even at 4096)
+constexpr int kTlDnBig = 3;  // (T = 16384: 8 waves measured 3% faster for the layer than 4)
 
 namespace {
 
@@ -594,7 +557,7 @@ namespace {
 int cfg_bm(int which) { return which >= 1 && which <= 3 ? 256 : 128; }
 int cfg_bn(int which) { return which >= 2 ? 256 : 128; }
 
-bool big_batch(int T, int K, int E) { return (long long)T * K >= (long long)FLINT_TL_BIG_ROWS * E; }
+bool big_batch(int T, int K, int E) { return (long long)T * K >= (long long)kTlBigRows * E; }
 
 // A dense layer (no routed experts) has T rows in every product, so its tiles
 // come in whole waves over the 256 CUs of an MI355X (one work-group per CU
@@ -613,13 +576,13 @@ bool dense_gu_big(int T, int Is)
 }
 int gu_cfg(int T, int K, int E, int Is)
 {
-    if (K == 0) return Is % 128 == 0 && dense_gu_big(T, Is) ? 3 : FLINT_TL_GU_SMALL;
-    return big_batch(T, K, E) ? FLINT_TL_GU_BIG : FLINT_TL_GU_SMALL;
+    if (K == 0) return Is % 128 == 0 && dense_gu_big(T, Is) ? 3 : kTlGuSmall;
+    return big_batch(T, K, E) ? kTlGuBig : kTlGuSmall;
 }
 int dn_cfg(int T, int K, int E)
 {
     if (K == 0) return 3;
-    return big_batch(T, K, E) ? FLINT_TL_DN_BIG : FLINT_TL_DN_SMALL;
+    return big_batch(T, K, E) ? kTlDnBig : kTlDnSmall;
 }
 
 template <int MODE, typename C>
@@ -716,7 +679,7 @@ hipError_t launch_router_tiled(const void *x, int T, int H, const void *router, 
     ta.bias = bias;
     ta.logits = logits;
     ta.ksplit = router_splits(T, H, E, true);
-    return launch_mode<ROUTER>(FLINT_TL_ROUTER, ta, stream, m);
+    return launch_mode<ROUTER>(0, ta, stream, m);
 }
 
 }  // namespace flint
