@@ -18,15 +18,28 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "flint_oracle.c")
-LIBRARY = os.path.join(_HERE, "liboracle.so")
+# FLINT_SANITIZE_DIR=<dir> selects a build in <dir> with AddressSanitizer and
+# UndefinedBehaviorSanitizer (clang, whose shared runtime the process must
+# preload: tests/sanitize_host.py runs the CPU suite that way).
+SANITIZE_DIR = os.environ.get("FLINT_SANITIZE_DIR")
+SANITIZE = bool(SANITIZE_DIR)
+LIBRARY = os.path.join(SANITIZE_DIR, "liboracle.so") if SANITIZE else os.path.join(_HERE, "liboracle.so")
+CLANG = "/opt/rocm/llvm/bin/clang"
 
 
 def compile_source(src: str, out: str) -> str:
     """Compile an oracle source file with gcc (-O2, IEEE double, no fast-math,
-    OpenMP over tokens) into a shared library at ``out``."""
+    OpenMP over tokens) into a shared library at ``out``; under FLINT_SANITIZE_DIR
+    with clang and the address and undefined-behaviour sanitizers instead
+    (undefined behaviour is fatal, as a memory error is)."""
     tmp = f"{out}.tmp{os.getpid()}"  # per process: parallel test workers may build at once
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-           "-std=c11", "-Wall", "-o", tmp, src, "-lm"]
+    if SANITIZE:
+        cmd = [CLANG, "-O1", "-g", "-fPIC", "-shared", "-fopenmp=libgomp", "-fno-fast-math", "-ffp-contract=off",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+               "-std=c11", "-Wall", "-o", tmp, src, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+               "-std=c11", "-Wall", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -13,7 +13,11 @@ import os
 import torch  # noqa: F401  (load order, see above)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(HERE, "libflint_moe.so")
+# FLINT_SANITIZE_DIR=<dir> loads the build in <dir> whose host code carries
+# AddressSanitizer and UndefinedBehaviorSanitizer (made by
+# tests/sanitize_host.py, which also preloads their runtime); its device code
+# is the same as the default build's.
+LIBRARY = os.path.join(os.environ.get("FLINT_SANITIZE_DIR") or HERE, "libflint_moe.so")
 
 _lib = None
 
