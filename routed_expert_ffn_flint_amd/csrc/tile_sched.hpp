@@ -1,5 +1,5 @@
 // Work-group scheduling and wait helpers of the LDS-staged expert products
-// (tiled.hip, gu_direct.hip).
+// (tiled.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
