@@ -138,11 +138,10 @@ def test_flint_layer_small_batches(T):
     """Flint-shaped layer (H=2048, 256 experts top-6, 512/1024 wide) at batch
     sizes around the decode kernels' range (up to 384 tokens; 385 takes the
     tiled kernels; up to 16 tokens top-k and dispatch share one work-group):
-    routing of every token, outputs of sampled tokens."""
+    routing and outputs of every token."""
     wl = inputs.Workload(f"flint_T{T}", T, 2048, 256, 6, 512, 1024, True, 5)
     w, x = _layer(wl)
-    sample = list(range(T)) if T <= 40 else list(np.random.default_rng(T).choice(T, 40, replace=False)) + [T - 1]
-    st = G.parity_sampled(wl, w, x, sample)
+    st = G.parity_sampled(wl, w, x, list(range(T)))
     _check_dispatch_of(wl, st["idx"])
     print(f"flint T={T}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
 
@@ -168,7 +167,9 @@ def test_largest_supported_shape(T):
     sampled ones)."""
     wl = inputs.Workload(f"max_T{T}", T, 8192, 32, 8, 4096, 4096, True, 9)
     w, x = _layer(wl)
-    sample = list(range(T)) if T <= 8 else [0, 1, T // 3, T // 2, T - 2, T - 1]
+    # (T = 600: 40 tokens spread over the batch and its two ends; the oracle
+    # spends ~2 GFLOP in double on each token of this shape)
+    sample = list(range(T)) if T <= 8 else sorted(set(np.linspace(0, T - 1, 40).astype(int).tolist()) | {1, T - 2})
     st = G.parity_sampled(wl, w, x, sample)
     print(f"max_T{T}: rel_err={st['rel_err']:.3g} near_ties={st['near_ties']}")
 
