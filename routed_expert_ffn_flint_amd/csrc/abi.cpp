@@ -72,7 +72,17 @@ int list_capacity(int T, int K, int E, int bm)
     return (int)(pairs / bm + nonempty + 1);
 }
 
-Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int eb, int shared_splits)
+// The intermediate arrays (h, y) start at a fixed phase within 4 KB against
+// the output buffer: 1 KB past it.  The combine reads rows of y while it
+// writes the same rows of the output, and its speed depends on where the two
+// fall against each other (measured, the Flint layer with the output on a
+// 4 KB boundary: T = 16384 combine 121 us at 1 KB, 127 at 512 bytes, 139 at
+// 0 and at 2 KB; T = 4096 27 us at 1 KB, 31 at 0).  Sizing (no base) reserves
+// the largest padding.
+constexpr size_t kPhasePeriod = 4096, kPhaseOffset = 1024;
+
+static Workspace plan_workspace_out(void *base, const void *out, int T, int H, int E, int K, int I, int Is, int eb,
+                                    int shared_splits)
 {
     Workspace w{};
     const size_t TK = (size_t)T * K;
@@ -93,6 +103,14 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
         off += align_up(bytes ? bytes : 1);
         return p;
     };
+    auto phase = [&]() {
+        if (!b) {
+            off += kPhasePeriod;
+            return;
+        }
+        const uintptr_t want = ((uintptr_t)out + kPhaseOffset) % kPhasePeriod;
+        off += ((want + kPhasePeriod - ((uintptr_t)b + off) % kPhasePeriod) % kPhasePeriod) / kAlign * kAlign;
+    };
     w.logits = (float *)take((size_t)router_splits(T, H, E, eb == 2) * T * E * 4);
     w.hist = (int32_t *)take((size_t)ntiles * E * 4);
     w.tile_base = (int32_t *)take((size_t)ntiles * E * 4);
@@ -106,9 +124,12 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     w.list1 = (int32_t *)take((size_t)cap1 * 8);
     w.list2 = (int32_t *)take((size_t)cap2 * 8);
     w.meta = (int32_t *)take(16);
+    phase();
     w.h_sorted = take(TK * I * eb);
     w.h_shared = take((size_t)T * Is * eb);
+    phase();
     w.y_sorted = (float *)take(TK * H * 4);
+    phase();
     w.y_shared = (float *)take((size_t)shared_splits * T * H * 4);
     if (tiles.tiled && K > 0) w.y_scale = (int8_t *)take(TK * (H / kYScaleCols));
     if (eb == 2 && K > 0 && T <= kFusedMaxT) {  // the fused decode kernel's own state
@@ -117,6 +138,11 @@ Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, 
     }
     w.bytes = off;
     return w;
+}
+
+Workspace plan_workspace(void *base, int T, int H, int E, int K, int I, int Is, int eb, int shared_splits)
+{
+    return plan_workspace_out(base, nullptr, T, H, E, K, I, Is, eb, shared_splits);
 }
 
 // On the streaming kernels a shared down item reduces over Is and a routed one
@@ -289,8 +315,8 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
     hipStream_t s = (hipStream_t)stream;
     const bool bf16 = d->dtype == FLINT_BF16;
     const int shared_splits = moe_shared_splits(d, T, e.mx4, fused);
-    Workspace w = plan_workspace(ws, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
-                                 elem_bytes(d), shared_splits);
+    Workspace w = plan_workspace_out(ws, out, T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
+                                     elem_bytes(d), shared_splits);
     // stage marks: router, top-k + dispatch, gate/up, down, combine
     Marks marks[5];
     if (events)
@@ -556,10 +582,10 @@ int dense_splits(const flint_dense_dims *d, int32_t T)
     return best;
 }
 
-Workspace dense_workspace(const flint_dense_dims *d, int32_t T, void *base)
+Workspace dense_workspace(const flint_dense_dims *d, int32_t T, void *base, const void *out = nullptr)
 {
-    return plan_workspace(base, T, d->hidden, 1, 0, 0, d->inter, d->dtype == FLINT_BF16 ? 2 : 4,
-                          dense_splits(d, T));
+    return plan_workspace_out(base, out, T, d->hidden, 1, 0, 0, d->inter, d->dtype == FLINT_BF16 ? 2 : 4,
+                              dense_splits(d, T));
 }
 
 }  // namespace
@@ -588,7 +614,7 @@ flint_status flint_dense_mlp(const flint_dense_dims *d, int32_t T, const void *x
     if (((uintptr_t)ws & (kAlign - 1)) != 0) return FLINT_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     const bool bf16 = d->dtype == FLINT_BF16;
-    Workspace w = dense_workspace(d, T, ws);
+    Workspace w = dense_workspace(d, T, ws, out);
     ExpertArgs e{};
     e.bf16 = bf16;
     e.T = T;

@@ -507,11 +507,14 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
 // ---------------------------------------------------------------------------
 // Host side
 
-constexpr int kTlBigRows = 256;  // mean rows per expert from which the big configurations are used
-constexpr int kTlGuSmall = 6;  // gate/up below that: 0 CfgSmall, 1 CfgWide, 6 CfgWideN (T = 4096: 290 -> 280 us)
-constexpr int kTlGuBig = 3;  // gate/up from there: 2 CfgBig, 3 CfgBig8 (or 0, 1)
+constexpr int kTlBigRows = 256;  // mean rows per expert from which the down product takes 256 x 256 tiles
+// Gate/up on 128 x 256 tiles (a routed layer at every size; a dense layer
+// unless its 256 x 256 tiles come in fewer waves, see dense_gu_big) (which: 0 CfgSmall, 1 CfgWide,
+// 2 CfgBig, 3 CfgBig8, 6 CfgWideN; T = 4096: 290 -> 280 us against CfgSmall;
+// T = 16384: 667 -> 625 us against CfgBig8, 879 with CfgBig, 946 with CfgWide).
+constexpr int kTlGuWide = 6;
 constexpr int kTlDnSmall = 6;  // (T = 2048: 128 x 256 tiles 154 -> 144 us; even at 4096)
-constexpr int kTlDnBig = 3;  // (T = 16384: 8 waves measured 3% faster for the layer than 4)
+constexpr int kTlDnBig = 3;  // (T = 16384: 8 waves measured 3% faster for the layer than 4; 128 x 256: 498 vs 478 us)
 
 namespace {
 
@@ -538,8 +541,8 @@ bool dense_gu_big(int T, int Is)
 }
 int gu_cfg(int T, int K, int E, int Is)
 {
-    if (K == 0) return Is % 128 == 0 && dense_gu_big(T, Is) ? 3 : kTlGuSmall;
-    return big_batch(T, K, E) ? kTlGuBig : kTlGuSmall;
+    if (K == 0) return Is % 128 == 0 && dense_gu_big(T, Is) ? 3 : kTlGuWide;
+    return kTlGuWide;
 }
 int dn_cfg(int T, int K, int E)
 {
