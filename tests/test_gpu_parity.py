@@ -422,6 +422,26 @@ def test_deterministic(name):
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+@pytest.mark.parametrize("T", [32, 600])
+def test_buffer_placement_does_not_change_results(T):
+    """The workspace's intermediate arrays are placed at a phase against the
+    output buffer: output and workspace at other offsets (the output 16-byte
+    aligned only) must give the same bits."""
+    wl = inputs.Workload(f"place_T{T}", T, 2048, 256, 6, 512, 1024, True, 7)
+    w, x = _layer(wl)
+    d = api.dims_of(wl)
+    need = api.flint_moe_workspace_bytes(d, T)
+    ref = torch.empty((T, d.hidden), dtype=torch.float32, device="cuda")
+    api.flint_moe_forward(d, x, w, ref, ws=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    big = torch.empty(T * d.hidden * 4 + 8192, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(need + 8192, dtype=torch.uint8, device="cuda")
+    for out_off, ws_off in ((16, 0), (272, 256), (1040, 3840), (4080, 1024)):
+        out = big[out_off:out_off + T * d.hidden * 4].view(torch.float32).view(T, d.hidden)
+        api.flint_moe_forward(d, x, w, out, ws=wsb[ws_off:ws_off + need])
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), (out_off, ws_off)
+
+
 def test_empty_batch_is_a_noop():
     wl = inputs.WORKLOADS["decode32"]
     d = api.dims_of(wl)
