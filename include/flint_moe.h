@@ -145,11 +145,11 @@ flint_status flint_moe_dispatch(const flint_moe_dims *dims, int32_t T, const int
  *   The result is deterministic: the same inputs give the same bits.
  *   Precision: h is stored in dims.dtype, every sum is float32.  At batch
  *   sizes served by the LDS-tiled kernels (bf16, T > 384) each routed
- *   expert's output row travels from the down product to the combine as fp16
- *   scaled by a power of two per 64 columns (the scale keeps every finite
- *   value in range), which adds at most 2^-11 of each term's magnitude: with
- *   weights summing to 1, at most 2^-11 of the largest routed output of the
- *   token. */
+ *   expert's output row, and the shared expert's, travels from the down
+ *   product to the combine as fp16 scaled by a power of two per 64 columns
+ *   (the scale keeps every finite value in range), which adds at most 2^-11
+ *   of each term's magnitude: with routed weights summing to 1, at most 2^-11
+ *   of the largest routed output of the token plus 2^-11 of the shared one. */
 flint_status flint_moe_forward(const flint_moe_dims *dims, int32_t T, const void *x,
                                const flint_moe_weights *weights, void *out,
                                flint_dtype out_dtype, int32_t *topk_idx_out,

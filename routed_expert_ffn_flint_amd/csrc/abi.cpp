@@ -131,7 +131,7 @@ static Workspace plan_workspace_out(void *base, const void *out, int T, int H, i
     w.y_sorted = (float *)take(TK * H * 4);
     phase();
     w.y_shared = (float *)take((size_t)shared_splits * T * H * 4);
-    if (tiles.tiled && K > 0) w.y_scale = (int8_t *)take(TK * (H / kYScaleCols));
+    if (tiles.tiled && K > 0) w.y_scale = (int8_t *)take((TK + T) * (H / kYScaleCols));
     if (eb == 2 && K > 0 && T <= kFusedMaxT) {  // the fused decode kernel's own state
         w.topk_q = (int32_t *)take((size_t)kFusedQueues * TK * 4);
         w.sync = (int32_t *)take((size_t)kFusedSyncWords * 4);

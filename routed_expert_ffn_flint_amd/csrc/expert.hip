@@ -226,7 +226,8 @@ __global__ __launch_bounds__(WaveGrid<SPLIT>::THREADS) void k_down(ExpertArgs a,
 
 // ---------------------------------------------------------------------------
 // out[t] = sum_k w[t][k] * y_sorted[slot_of[t*K+k]] + y_shared[t]   (fixed order)
-// Y16: y_sorted holds fp16 values times 2^y_scale (see ExpertArgs::y16).
+// Y16: y_sorted and a single y_shared hold fp16 values times 2^y_scale (see
+// ExpertArgs::y16).
 template <bool Y16>
 __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 {
@@ -267,9 +268,18 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
                 y[k] = *reinterpret_cast<const f32x4 *>(a.y_sorted + (size_t)slots[k] * H + c);
         }
     }
-    const f32x4 ys = a.Is > 0 ? *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c)
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
     const int nsplit = a.shared_splits > 1 ? a.shared_splits : 1;
+    f32x4 ys = {0.f, 0.f, 0.f, 0.f};
+    if (Y16 && a.Is > 0 && nsplit == 1) {  // fp16 times 2^exponent, the exponents after the T*K routed rows
+        typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+        const h16x4 v = *reinterpret_cast<const h16x4 *>(reinterpret_cast<const _Float16 *>(a.y_shared) +
+                                                         (size_t)t * H + c);
+        const int sc = a.y_scale[((size_t)a.T * K + t) * (H / kYScaleCols) + c / kYScaleCols];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ys[j] = ldexpf((float)v[j], sc);
+    } else if (a.Is > 0) {
+        ys = *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {

@@ -98,7 +98,7 @@ struct Workspace {
     void *h_shared;       // [T][Is] dtype
     float *y_sorted;      // [T*K][H] float32, or fp16 (with y_scale) on the tiled kernels
     float *y_shared;      // [T][H]
-    int8_t *y_scale;      // [T*K][H/64]: power-of-two exponents of fp16 y_sorted
+    int8_t *y_scale;      // [T*K + T][H/64]: power-of-two exponents of fp16 y_sorted, then of fp16 y_shared
     int32_t *topk_q;      // fused decode: [queues][T][K] per-queue copies of the selection
     int32_t *sync;        // fused decode: kFusedSyncWords counters
     size_t bytes;         // total bytes needed
@@ -146,7 +146,8 @@ struct DispatchArgs {
     int32_t *list1, *list2, *meta;
     int bm1, bm2;
     // the exponents of the tiled down product's fp16 outputs, cleared by the
-    // dispatch's scatter kernel ([T*K][scale_cols] bytes; null: none)
+    // dispatch's scatter kernel ([T*K + T][scale_cols] bytes: the routed
+    // rows, then the shared expert's; null: none)
     int8_t *y_scale;
     int scale_cols;
 };
@@ -167,7 +168,9 @@ struct ExpertArgs {
     float *y_sorted, *y_shared;
     // The tiled down product stores routed rows of y_sorted as fp16 times
     // 2^y_scale[slot][c / 64] (an exponent per row and 64 columns, 0 unless
-    // the row's 64 values reach 2^15); the combine reads them back.
+    // the row's 64 values reach 2^15), and the shared expert's rows of
+    // y_shared likewise with exponents y_scale[T*K + t]; the combine reads
+    // them back.
     bool y16;
     int8_t *y_scale;
     // The shared expert's down product split over its reduction into this many

@@ -527,8 +527,11 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(DispatchArgs a)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= a.T * a.K) return;
-    if (a.y_scale)  // row i of the fp16 output exponents starts at 0 (the tiled path has T > 256: this kernel runs)
+    if (a.y_scale) {  // the fp16 output exponents start at 0 (the tiled path has T > 256: this kernel runs)
         for (int c = 0; c < a.scale_cols; ++c) a.y_scale[(size_t)i * a.scale_cols + c] = 0;
+        if (i < a.T)  // the shared expert's rows follow the T*K routed ones
+            for (int c = 0; c < a.scale_cols; ++c) a.y_scale[((size_t)a.T * a.K + i) * a.scale_cols + c] = 0;
+    }
     const int t = i / a.K;
     const int e = a.topk_idx[i];
     const int tile = t / kTopkTile;

@@ -398,7 +398,10 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
     // stores.
     constexpr int kGroups = (MODE == DOWN) ? NB / 4 : 1;
     static_assert(MODE != DOWN || NB % 4 == 0, "64-column exponent groups");
-    const bool y16 = MODE == DOWN && !shared && a.y16;
+    // (a routed layer's shared rows too: its tiled path keeps one y_shared array)
+    const bool y16 = MODE == DOWN && a.y16 && (!shared || a.shared_splits <= 1);
+    // exponent row of output row r: routed slots first, then the shared rows
+    const size_t scale_row0 = shared ? (size_t)a.T * a.K : 0;
     constexpr bool kStaged = MODE == DOWN && C::WN == 64;
     constexpr int kWavesPerStage = C::STAGE_ELEMS / (C::WM * C::WN);
     static_assert(!kStaged || C::WAVES <= STAGES * kWavesPerStage, "a wave-tile region of LDS per wave");
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
                     for (int g = 0; g < kGroups; ++g) {
                         const int c = nt * BN + wn * C::WN + g * 64;
                         if (scaled && (lane & 15) == 0 && c < H)
-                            a.y_scale[(size_t)r * (H / kYScaleCols) + c / kYScaleCols] = (int8_t)sexp[g];
+                            a.y_scale[(scale_row0 + r) * (H / kYScaleCols) + c / kYScaleCols] = (int8_t)sexp[g];
                     }
                 } else {
 #pragma unroll

@@ -398,18 +398,23 @@ def test_route_extreme_logits(T, via, regime):
         G.check_output(out.cpu().numpy(), ref, f"extreme_{regime}")
 
 
+@pytest.mark.parametrize("which", ["routed", "shared", "both"])
 @pytest.mark.parametrize("scale_log2", [20, 40])
-def test_tiled_routed_outputs_beyond_fp16_range(scale_log2):
-    """On the tiled kernels the routed outputs travel to the combine as fp16
-    with a power-of-two exponent per row and 64 columns.  Down weights of half
-    the experts multiplied by 2^20 or 2^40 (exact in bf16) put routed outputs
-    far past fp16's largest value (65504) while the others stay small: the
-    result must be finite and within the bar on every token."""
-    wl = inputs.custom(f"y16_big_{scale_log2}", 600, 256, 16, 4, 128, 128, True, seed=23)
+def test_tiled_outputs_beyond_fp16_range(scale_log2, which):
+    """On the tiled kernels the routed and the shared expert's outputs travel
+    to the combine as fp16 with a power-of-two exponent per row and 64
+    columns.  Down weights of half the experts (routed), of the shared expert,
+    or both, multiplied by 2^20 or 2^40 (exact in bf16), put those outputs far
+    past fp16's largest value (65504) while the others stay small: the result
+    must be finite and within the bar on every token."""
+    wl = inputs.custom(f"y16_big_{scale_log2}_{which}", 600, 256, 16, 4, 128, 128, True, seed=23)
     w, x = _layer(wl)
-    w["down"][::2].mul_(2.0 ** scale_log2)
+    if which in ("routed", "both"):
+        w["down"][::2].mul_(2.0 ** scale_log2)
+    if which in ("shared", "both"):
+        w["shared_down"].mul_(2.0 ** scale_log2)
     st = G.parity_full(wl, w, x)
-    print(f"y16 x2^{scale_log2}: rel_err={st['rel_err']:.3g}")
+    print(f"y16 {which} x2^{scale_log2}: rel_err={st['rel_err']:.3g}")
 
 
 @pytest.mark.parametrize("name", ["decode32", "prefill4096"])
