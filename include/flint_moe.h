@@ -278,7 +278,7 @@ flint_status flint_dense_mlp(const flint_dense_dims *dims, int32_t T, const void
  * Results are those of flint_moe_forward, bit for bit.
  *   - A shape whose flint_moe_workspace_bytes(dims, T) exceeds
  *     FLINT_STATIC_SCRATCH_BYTES is refused with FLINT_WORKSPACE_TOO_SMALL
- *     (48 MiB: the Flint layer up to T = 750 tokens), before any launch.
+ *     (48 MiB: the Flint layer up to T = 751 tokens), before any launch.
  *   - Every call on one GPU uses that GPU's one array: calls that overlap on a
  *     GPU (several streams or threads at once) race and give undefined results;
  *     serialise them, or use flint_moe_forward with a workspace per stream.

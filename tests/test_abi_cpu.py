@@ -233,6 +233,9 @@ def test_forward_static_refusals(lib):
     assert re.search(r"FLINT_STATIC_SCRATCH_BYTES \(\(size_t\)48 << 20\)", open(HEADER).read())
     T_max = max(T for T in range(1, 2048) if api.flint_moe_workspace_bytes(d, T) <= limit)
     assert T_max >= 512  # the decode batches and the 256-token stack fit
+    # the largest batch the header states for the Flint layer
+    stated = re.search(r"the Flint layer up to T = (\d+) tokens", open(HEADER).read())
+    assert stated and int(stated.group(1)) == T_max
     assert _forward_static(lib, d, T_max + 1) == api.WORKSPACE_TOO_SMALL
     assert _forward_static(lib, d, 100_000) == api.WORKSPACE_TOO_SMALL
 
