@@ -58,13 +58,13 @@ CSRC = os.path.join(ROOT, "routed_expert_ffn_flint_amd", "csrc")
 KERNEL_SOURCES = {
     "k_expert_stream": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream.hip"],
     "k_expert_stream_mx4": ["common.hpp", "gemm_core.hpp", "launch.hpp", "stream_mx4.hip"],
-    "k_tiled": ["common.hpp", "gemm_core.hpp", "launch.hpp", "tiled.hip"],
+    "k_tiled": ["common.hpp", "gemm_core.hpp", "launch.hpp", "tile_sched.hpp", "tiled.hip"],
     "k_fused_decode": ["common.hpp", "gemm_core.hpp", "launch.hpp", "topk.hpp", "fused.hip"],
 }
-# largest bf16 batches the library serves with the streaming kernels (a MoE
-# layer, a dense layer); larger ones go to the tiled kernels
+# largest bf16 batch of a MoE layer the library serves with the streaming
+# kernels; larger ones go to the tiled kernels (a bf16 dense layer takes the
+# tiled kernels at every size)
 STREAM_MAX_T = 384
-DENSE_STREAM_MAX_T = 128
 
 
 def parse():
@@ -395,7 +395,7 @@ def bench_dense(args, wl):
     layer_bytes = 3 * I * H * eb + T * H * eb + T * H * 4
     layer_flops = 6 * T * I * H
     big = gu_flops / gu_bytes >= RIDGE  # arithmetic intensity of the gate/up kernel
-    kernel = "k_expert_stream" if T <= DENSE_STREAM_MAX_T else "k_tiled"
+    kernel = "k_tiled"
     digest = sources_digest(kernel)
     kname = f"{kernel}<gate/up> (gate/up GEMM + SwiGLU of the dense layer)"
     traffic = counters_traffic(kernel, wl.name, digest)

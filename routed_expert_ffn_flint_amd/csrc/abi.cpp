@@ -568,9 +568,10 @@ flint_status check_dense(const flint_dense_dims *d, int32_t T)
 }
 
 // A dense layer runs on the expert kernels as a layer with no routed experts
-// (K = 0, I = 0) whose shared expert has the dense width.  On the streaming
-// kernels its down product has only H/32 column tiles per 32 rows, so the
-// reduction is split into `dense_splits` partial arrays that the combine adds.
+// (K = 0, I = 0) whose shared expert has the dense width.  Its down product has
+// few column tiles per row tile (H/64 on the 32-row tiles, H/32 on the
+// streaming kernels), so the reduction is split into `dense_splits` partial
+// arrays that the combine adds.
 int dense_splits(const flint_dense_dims *d, int32_t T)
 {
     if (expert_tiles_for(T, d->hidden, 1, 0, 0, d->inter, d->dtype == FLINT_BF16).tiled)

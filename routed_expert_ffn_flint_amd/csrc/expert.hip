@@ -324,6 +324,9 @@ ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf1
     const bool tiled = tiled_eligible(T, K, E, H, I, Is, bf16);
     const int small_max = tiled ? (K > 0 ? kTiledFromT : kDenseTiledFromT) - 1 : kStreamMaxT;
     if (T <= small_max) {
+        // a dense bf16 layer: the tiled kernels' 32-row configurations (faster
+        // than weight streaming at every T measured, 1 to 128)
+        if (tiled && K == 0) return ExpertTiles{32, 0, 32, 0, false, false, true};
         if (stream_eligible(T, H, I, Is))
             return ExpertTiles{stream_bm1(T, K), 0, stream_bm2(), 0, true, true, false};
         // Small batches (decode): split-k kernels over 32-row tiles, so that one

@@ -1,5 +1,5 @@
-// LDS-tiled GEMMs for large batches (prefill): the grouped expert products and
-// the router.
+// LDS-tiled GEMMs: the grouped expert products and the router for large
+// batches (prefill), and a dense bf16 layer's products at every batch size.
 //
 // Layer (serving-kit review, "The architecture, from the config"; release news
 // page, "What runs on each token"): a sigmoid router over the experts, then K
@@ -90,6 +90,16 @@ using CfgWide = Cfg<256, 128, 128, 64, 32, 6>;  // 4 waves
 using CfgBig = Cfg<256, 256, 128, 128, 32, 4>;  // 4 waves
 using CfgBig8 = Cfg<256, 256, 128, 64, 32, 4>;  // 8 waves
 using CfgWideN = Cfg<128, 256, 64, 64, 64, 3>;  // 8 waves
+// A dense layer at decode sizes (T < kDenseTiledFromT): 32-row tiles and
+// rings of 64-wide slices, the weights streaming through LDS with several
+// slices in flight per work-group; gate/up 32 gate + 32 up channels on two
+// waves (6 stages, two work-groups per CU, up to 64 rows; beyond, 4 stages and
+// three per CU for the extra row tiles: T = 128 gate/up 31.8 -> 24.1 us, T = 64
+// 18.3 -> 19.0), down 64 columns on one wave over a split of the width.
+using CfgDecGu = Cfg<32, 64, 32, 32, 64, 6>;    // 2 waves
+using CfgDecGu4 = Cfg<32, 64, 32, 32, 64, 4>;   // 2 waves
+using CfgDecDn = Cfg<32, 64, 32, 64, 64, 6>;    // 1 wave
+constexpr int kDecGuRows6 = 64;  // largest batch on CfgDecGu
 
 enum Mode { GATE_UP = 0, DOWN = 1, ROUTER = 2 };
 
@@ -606,6 +616,15 @@ bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16)
 // 349 -> 342 (2); at 8192 one split (256 tiles) is best.
 int tiled_dense_splits(int T, int H, int Is)
 {
+    if (T < kDenseTiledFromT) {
+        // 32-row tiles of 64 columns: H/64 per row tile, too few to fill the CUs
+        // alone; the most splits up to 8 whose slices stay whole (T = 32, width
+        // 6144: 8 splits, 256 items)
+        int best = 1;
+        for (int s = 2; s <= 8; ++s)
+            if (Is % (CfgDecDn::BK * s) == 0) best = s;
+        return best;
+    }
     const long long tiles = (long long)(T + 255) / 256 * ((H + 255) / 256);
     int s = 1;
     while (s < 8 && tiles * (2 * s) <= kDenseCus && Is % (64 * 2 * s) == 0) s *= 2;
@@ -619,6 +638,17 @@ hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const M
 {
     TiledArgs ta{};
     ta.e = a;
+    if (a.K == 0 && a.T < kDenseTiledFromT) {
+        // a dense layer at decode sizes (layer times measured on the dense layer,
+        // H = 2048, width 6144, against the weight-streaming kernels: T = 1
+        // 27.6 -> 25.4 us, T = 32 35.2 -> 28.6, T = 64 50.6 -> 35.6, T = 128
+        // 73.5 -> 48.6)
+        const Marks m = marks ? marks[0] : Marks{};
+        const hipError_t err = a.T <= kDecGuRows6 ? launch_cfg<GATE_UP, CfgDecGu>(ta, stream, m)
+                                                  : launch_cfg<GATE_UP, CfgDecGu4>(ta, stream, m);
+        if (err != hipSuccess) return err;
+        return launch_cfg<DOWN, CfgDecDn>(ta, stream, marks ? marks[1] : Marks{});
+    }
     const hipError_t err = launch_mode<GATE_UP>(gu_cfg(a.T, a.K, a.E, a.Is), ta, stream, marks ? marks[0] : Marks{});
     if (err != hipSuccess) return err;
     return launch_mode<DOWN>(dn_cfg(a.T, a.K, a.E), ta, stream, marks ? marks[1] : Marks{});

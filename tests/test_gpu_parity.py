@@ -570,16 +570,16 @@ def test_mx4_largest_widths():
 
 DENSE_CASES = [
     # name,         T,    H,    I,    bf16
-    ("d_t1",        1,    128,  192,  True),
-    ("d_t33",       33,   256,  320,  True),
+    ("d_t1",        1,    128,  192,  True),    # 32-row tiled configurations, down split 3 ways
+    ("d_t33",       33,   256,  320,  True),    # two 32-row tiles, the second ragged; down split 5 ways
     ("d_t7_f32",    7,    128,  64,   False),
-    ("d_t128",      128,  256,  512,  True),    # the largest dense batch on the streaming kernels
-    ("d_t129",      129,  256,  512,  True),    # the smallest on the tiled kernels, down split 8 ways
+    ("d_t128",      128,  256,  512,  True),    # the largest dense batch on the 32-row tiles
+    ("d_t129",      129,  256,  512,  True),    # the smallest on the large-batch tiles, down split 8 ways
     ("d_t600",      600,  256,  512,  True),    # large-batch (tiled) kernels, down split 8 ways
     ("d_t1000",     1000, 256,  6144, True),    # 256 x 256 gate/up tiles, ragged last tile
     ("d_t700_f32",  700,  128,  128,  False),   # float32 large-batch kernels
     ("d_flint32",   32,   2048, 6144, True),    # the dense layer's width, decode batch (down split 8 ways)
-    ("d_t20_s6",    20,   1024, 1536, True),    # down split 6 ways
+    ("d_t20_w1536", 20,   1024, 1536, True),    # down split 8 ways, 192 of the width each
     ("d_t40_f32",   40,   256,  512,  False),   # float32 on the streaming kernels
     ("d_t300_f32",  300,  256,  768,  False),   # float32 on the streaming kernels, down split
 ]
@@ -696,7 +696,7 @@ GRAPH_CASES = [
     ("decode32",      32),    # the decode batch
     ("prefill4096",   600),   # three-kernel dispatch, tiled experts
     ("decode32_mx4",  32),    # MXFP4 expert weights
-    ("dense32",       32),    # dense layer, streaming
+    ("dense32",       32),    # dense layer, 32-row tiles, split down product
     ("dense4096",     600),   # dense layer, tiled, split down product
 ]
 
