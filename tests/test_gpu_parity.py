@@ -579,6 +579,7 @@ DENSE_CASES = [
     ("d_t1000",     1000, 256,  6144, True),    # 256 x 256 gate/up tiles, ragged last tile
     ("d_t700_f32",  700,  128,  128,  False),   # float32 large-batch kernels
     ("d_flint32",   32,   2048, 6144, True),    # the dense layer's width, decode batch (down split 8 ways)
+    ("d_flint100",  100,  2048, 6144, True),    # four 32-row tiles, the last ragged; the 4-stage gate/up ring
     ("d_t20_w1536", 20,   1024, 1536, True),    # down split 8 ways, 192 of the width each
     ("d_t40_f32",   40,   256,  512,  False),   # float32 on the streaming kernels
     ("d_t300_f32",  300,  256,  768,  False),   # float32 on the streaming kernels, down split
@@ -619,7 +620,7 @@ def test_dense_every_token(case):
     assert torch.equal(out.view(torch.int32), again.view(torch.int32))  # deterministic
 
 
-@pytest.mark.parametrize("shape", [(45, 256, 384), (24, 1024, 1536)])  # one combine input; six partial sums
+@pytest.mark.parametrize("shape", [(45, 256, 704), (24, 1024, 1536)])  # one combine input; eight partial sums
 def test_dense_bf16_output(shape):
     T, H, I = shape
     wl = inputs.custom("d_bf16out", T, H, 0, 0, I, 0, True, seed=2, dense=True)
@@ -630,7 +631,7 @@ def test_dense_bf16_output(shape):
 @pytest.mark.parametrize("T", [5, 200])
 def test_dense_largest_widths(T):
     """The dense layer at the largest widths it takes (H = 8192, width 16384):
-    T = 5 on the streaming kernels (every token), T = 200 on the tiled ones
+    T = 5 on the 32-row tiles (every token), T = 200 on the large-batch tiles
     (sampled tokens)."""
     wl = inputs.custom(f"d_max_T{T}", T, 8192, 0, 0, 16384, 0, True, seed=17, dense=True)
     w, x = _dense(wl)
