@@ -64,7 +64,7 @@ KERNEL_SOURCES = {
 # largest bf16 batch of a MoE layer the library serves with the streaming
 # kernels; larger ones go to the tiled kernels (a bf16 dense layer takes the
 # tiled kernels at every size)
-STREAM_MAX_T = 384
+STREAM_MAX_T = 159
 
 
 def parse():

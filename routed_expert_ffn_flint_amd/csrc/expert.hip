@@ -321,19 +321,17 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
 // ---------------------------------------------------------------------------
 ExpertTiles expert_tiles_for(int T, int H, int E, int K, int I, int Is, bool bf16)
 {
-    const bool tiled = tiled_eligible(T, K, E, H, I, Is, bf16);
-    const int small_max = tiled ? (K > 0 ? kTiledFromT : kDenseTiledFromT) - 1 : kStreamMaxT;
-    if (T <= small_max) {
-        // a dense bf16 layer: the tiled kernels' 32-row configurations (faster
-        // than weight streaming at every T measured, 1 to 128)
-        if (tiled && K == 0) return ExpertTiles{32, 0, 32, 0, false, false, true};
+    // the LDS-tiled kernels: a bf16 dense layer at every T, a MoE layer from
+    // kTiledFromT rows (their tile rows depend on T: tiled_bm1 / tiled_bm2)
+    if (tiled_eligible(T, K, E, H, I, Is, bf16) && (K == 0 || T >= kTiledFromT))
+        return ExpertTiles{tiled_bm1(T, K, E, Is), 0, tiled_bm2(T, K, E), 0, false, false, true};
+    if (T <= kStreamMaxT) {
         if (stream_eligible(T, H, I, Is))
             return ExpertTiles{stream_bm1(T, K), 0, stream_bm2(), 0, true, true, false};
         // Small batches (decode): split-k kernels over 32-row tiles, so that one
         // tile holds every row an expert gets and each weight is read once.
         return ExpertTiles{32, kGuNb / 2 * 16, 32, kDnNb * 16, true, false, false};
     }
-    if (tiled) return ExpertTiles{tiled_bm1(T, K, E, Is), 0, tiled_bm2(T, K, E), 0, false, false, true};
     return ExpertTiles{128, 64, 128, 128, false, false, false};
 }
 

@@ -47,11 +47,16 @@ constexpr int kMaxTopK = 8;
 // Largest batch the persistent weight-streaming expert kernels (and the
 // split-k small-batch kernels) serve.
 constexpr int kStreamMaxT = 512;
-// Where the LDS-tiled kernels take over when the shape allows them (bf16):
-// from 385 rows for a MoE layer (Flint shape: T = 512 401 -> 385 us; even at
-// 384), from 129 rows for a dense layer, whose weights the streaming kernels
-// read again for every 32 rows (T = 192: 108 -> 74 us; even at 128).
-constexpr int kTiledFromT = 385;
+// Where the LDS-tiled kernels take over when the shape allows them (bf16).
+// A MoE layer: from 160 rows on 16-row tiles (Flint shape, layer time against
+// the weight-streaming kernels: T = 192 328 -> 313 us, 256 338 -> 318, 384
+// 376 -> 346; even at 128, slower at 64), from 513 rows on the 128- and
+// 256-row tiles (T = 640: 398 -> 373 us; at 448 and 512 the 16-row tiles are
+// 1-2% faster).  A dense layer at every T: 32-row tiles below 129 rows, the
+// large tiles from there (its weights the streaming kernels read again for
+// every 32 rows).
+constexpr int kTiledFromT = 160;
+constexpr int kLargeTilesFromT = 513;
 constexpr int kDenseTiledFromT = 129;
 
 // The persistent fused decode kernel (fused.hip): queues (work-group classes),
@@ -146,8 +151,9 @@ struct DispatchArgs {
     int32_t *list1, *list2, *meta;
     int bm1, bm2;
     // the exponents of the tiled down product's fp16 outputs, cleared by the
-    // dispatch's scatter kernel ([T*K + T][scale_cols] bytes: the routed
-    // rows, then the shared expert's; null: none)
+    // dispatch (its scatter kernel, or the one work-group of a single tile)
+    // ([T*K + T][scale_cols] bytes: the routed rows, then the shared expert's;
+    // null: none)
     int8_t *y_scale;
     int scale_cols;
 };

@@ -384,6 +384,15 @@ __device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, Tile
     }
     const int off = finish_offsets_and_lists(hcount, E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2,
                                              a.meta, L.lds);
+    if (a.y_scale) {
+        // the fp16 output exponents start at 0 (for several tiles the scatter
+        // kernel clears them): the T*K routed rows and the T shared rows
+        // (16 bytes a store: the workspace's arrays start 256-byte aligned)
+        const int n = (a.T * K + a.T) * a.scale_cols;
+        uint4 *y16 = reinterpret_cast<uint4 *>(a.y_scale);
+        for (int i = threadIdx.x; i < n / 16; i += NT) y16[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = n / 16 * 16 + threadIdx.x; i < n; i += NT) a.y_scale[i] = 0;
+    }
     if (threadIdx.x < E) L.offs[threadIdx.x] = off;
     __syncthreads();
 #pragma unroll
@@ -527,7 +536,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(DispatchArgs a)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= a.T * a.K) return;
-    if (a.y_scale) {  // the fp16 output exponents start at 0 (the tiled path has T > 256: this kernel runs)
+    if (a.y_scale) {  // the fp16 output exponents start at 0
         for (int c = 0; c < a.scale_cols; ++c) a.y_scale[(size_t)i * a.scale_cols + c] = 0;
         if (i < a.T)  // the shared expert's rows follow the T*K routed ones
             for (int c = 0; c < a.scale_cols; ++c) a.y_scale[((size_t)a.T * a.K + i) * a.scale_cols + c] = 0;

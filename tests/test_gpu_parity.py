@@ -56,7 +56,7 @@ SMALL = [
     ("t24_e256_k8", 24, 2048, 256, 8, 512, 1024, True, True),  # the most experts and the largest K
     ("t64_k1",    64, 128, 16, 1, 128, 64,  True,  True),
     ("t100_f32",  100, 128, 24, 4, 64, 128, False, True),
-    ("t300",      300, 256, 64, 6, 128, 128, True, False),   # two dispatch tiles
+    ("t300",      300, 256, 64, 6, 128, 128, True, False),   # two dispatch tiles, 16-row tiles
     ("t600_f32",  600, 128, 16, 2, 64, 64,  False, False),
     ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
     ("t2100_big", 2100, 256, 16, 4, 128, 128, True, True),   # 256-row tiles, router split over H
@@ -133,12 +133,13 @@ def test_decode32_every_token():
           f"distinct experts={len(np.unique(st['idx']))}")
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 17, 33, 200, 384, 385, 512])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 33, 159, 160, 256, 257, 512, 513])
 def test_flint_layer_small_batches(T):
     """Flint-shaped layer (H=2048, 256 experts top-6, 512/1024 wide) at batch
-    sizes around the decode kernels' range (up to 384 tokens; 385 takes the
-    tiled kernels; up to 16 tokens top-k and dispatch share one work-group):
-    routing and outputs of every token."""
+    sizes around the kernels' boundaries (weight streaming up to 159 tokens,
+    16-row tiles from 160 to 512, the large tiles from 513; up to 16 tokens
+    top-k and dispatch share one work-group, up to 256 the dispatch is one
+    work-group): routing and outputs of every token."""
     wl = inputs.Workload(f"flint_T{T}", T, 2048, 256, 6, 512, 1024, True, 5)
     w, x = _layer(wl)
     st = G.parity_sampled(wl, w, x, list(range(T)))
@@ -695,6 +696,7 @@ GRAPH_CASES = [
     # workload,       T
     ("decode32",      8),     # one-launch top-k + dispatch, streaming experts
     ("decode32",      32),    # the decode batch
+    ("decode32",      200),   # one-work-group dispatch, 16-row tiles
     ("prefill4096",   600),   # three-kernel dispatch, tiled experts
     ("decode32_mx4",  32),    # MXFP4 expert weights
     ("dense32",       32),    # dense layer, 32-row tiles, split down product
