@@ -37,6 +37,7 @@ Prints ONE JSON line.  Beside the headline throughput:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import hashlib
 import json
@@ -73,6 +74,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode32")
+    p.add_argument("--tokens", type=int, default=None,
+                   help="tokens per step instead of the workload's own (other batch sizes of the same layer)")
     p.add_argument("--copies", type=int, default=4, help="weight copies rotated (single-layer workloads)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -463,6 +466,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     lib = _lib.load()
     wl = inputs.WORKLOADS[args.workload]
+    if args.tokens is not None:
+        if args.tokens < 1:
+            raise SystemExit("--tokens must be at least 1")
+        wl = dataclasses.replace(wl, T=args.tokens)
     if wl.dense:
         bench_dense(args, wl)
         return

@@ -10,9 +10,9 @@
 //   - a fixed grid of work-groups (a few per CU) walks the work items with a
 //     static stride, so per-group setup is paid once, not per tile;
 //   - each work-group first copies the dispatch tables (tile list, expert
-//     offsets) into LDS, so looking up an item's expert and rows costs LDS
-//     reads only (an item's tokens are read from the expert-sorted list in
-//     global memory when the item is set up, one item ahead);
+//     offsets, and for gate/up the expert-sorted token list) into LDS, so
+//     setting up an item costs LDS reads only and never waits on the
+//     vector-memory counter, which would also wait for the weights in flight;
 //   - each wave streams its quarter of the reduction dimension in batches of U
 //     32-wide slices, the next batch (of this item or of the next one) issued
 //     before the current batch's MFMAs, so weight loads stay in flight across
@@ -49,22 +49,43 @@ namespace {
 
 constexpr int kWaves = 4;
 
-// Dispatch tables in LDS: list (expert, first slot) pairs, offsets[E+1].
-struct Tables {
-    int32_t *list;
-    int32_t *offsets;
-    int nlist;
+// Dispatch tables in the kernel's dynamic LDS: the tile list's (expert,
+// first slot) pairs at [0, 2 nlist), the expert offsets (E + 1) after them, and
+// for gate/up the token of each slot (T K) after those.  The kernel indexes
+// the LDS array itself, never a pointer into it: read through a pointer kept
+// in a struct, the offsets had become flat loads, and the wait of a flat load
+// (like that of a global load of the token list) also waits for every weight
+// load in flight, so each item's setup drained the stream.
+struct TableLayout {
+    int nlist, offsets, tokens;  // list length; word index of the offsets and of the tokens
 };
 
-__device__ __forceinline__ Tables load_tables(const ExpertArgs &a, const int32_t *glist, int nlist, int32_t *lds)
+__device__ __forceinline__ TableLayout load_tables(const ExpertArgs &a, const int32_t *glist, int nlist,
+                                                   bool tokens, int32_t *lds)
 {
-    Tables t;
-    t.nlist = nlist;
-    t.list = lds;
-    t.offsets = lds + 2 * nlist;
-    for (int i = threadIdx.x; i < 2 * nlist; i += blockDim.x) t.list[i] = glist[i];
-    if (a.K > 0)  // a dense layer (K = 0) has shared items only and no dispatch tables
-        for (int i = threadIdx.x; i <= a.E; i += blockDim.x) t.offsets[i] = a.offsets[i];
+    TableLayout t{nlist, 2 * nlist, 2 * nlist + a.E + 1};
+    // the three arrays as one range of words (a dense layer, K = 0, has shared
+    // items only and no dispatch tables), each thread's loads all issued
+    // before the first is waited for
+    const int n_off = a.K > 0 ? a.E + 1 : 0;
+    const int total = t.offsets + n_off + (tokens && a.K > 0 ? a.T * a.K : 0);
+    constexpr int kPer = 4;
+    for (int i0 = threadIdx.x; i0 < total; i0 += kPer * blockDim.x) {
+        int v[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = min(i0 + u * (int)blockDim.x, total - 1);
+            const int32_t *src = i < t.offsets ? glist + i
+                                 : i < t.tokens ? a.offsets + (i - t.offsets)
+                                                : a.sorted_token + (i - t.tokens);
+            v[u] = *src;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = i0 + u * (int)blockDim.x;
+            if (i < total) lds[i] = v[u];
+        }
+    }
     __syncthreads();
     return t;
 }
@@ -100,7 +121,7 @@ __global__ __launch_bounds__(256, GATE_UP ? kStWgs1 : kStWgs2) void k_expert_str
     const int kg = (lane >> 4) * 8;
     const int H = a.H;
     const int nlist = GATE_UP ? (a.K > 0 ? a.meta[0] : 0) : (a.K > 0 ? a.meta[1] : 0);
-    const Tables tab = load_tables(a, GATE_UP ? a.list1 : a.list2, nlist, dyn_lds);
+    const TableLayout tab = load_tables(a, GATE_UP ? a.list1 : a.list2, nlist, GATE_UP, dyn_lds);
 
     const int ntn_shared = GATE_UP ? a.Is / BN : (H + BN - 1) / BN;
     const int ntn_routed = GATE_UP ? a.I / BN : (H + BN - 1) / BN;
@@ -133,9 +154,9 @@ __global__ __launch_bounds__(256, GATE_UP ? kStWgs1 : kStWgs2) void k_expert_str
             const int r = item - n_shared_items;
             const int entry = r / ntn_routed;
             nt = r % ntn_routed;
-            e = tab.list[2 * entry];
-            it.row0 = tab.list[2 * entry + 1];
-            it.row_end = tab.offsets[e + 1];
+            e = dyn_lds[2 * entry];
+            it.row0 = dyn_lds[2 * entry + 1];
+            it.row_end = dyn_lds[tab.offsets + e + 1];
             it.kdim = GATE_UP ? H : a.I;
             klen = it.kdim;
             wa = GATE_UP ? (const S *)a.gate + (size_t)e * a.I * H : (const S *)a.down + (size_t)e * H * a.I;
@@ -165,7 +186,7 @@ __global__ __launch_bounds__(256, GATE_UP ? kStWgs1 : kStWgs2) void k_expert_str
             int r = it.row0 + m * 16 + (lane & 15);
             if (r >= it.row_end) r = it.row0;  // rows past the tile repeat its first row (cache hits)
             if (GATE_UP) {
-                const int tok = it.shared ? r : a.sorted_token[r];
+                const int tok = it.shared ? r : dyn_lds[tab.tokens + r];
                 it.a[m] = (const S *)a.x + (size_t)tok * H + kg;
             } else {
                 it.a[m] = (it.shared ? (const S *)a.h_shared : (const S *)a.h_sorted) + (size_t)r * it.kdim + kg;
@@ -326,7 +347,7 @@ static hipError_t launch_stream_t(const ExpertArgs &a, hipStream_t stream, const
     const int ns2 = a.Is > 0 ? (a.T + bm2 - 1) / bm2 * ((a.H + bn2 - 1) / bn2) * nsplit : 0;
     const int max1 = ns1 + cap1 * (a.I / bn1);
     const int max2 = ns2 + cap2 * ((a.H + bn2 - 1) / bn2);
-    const size_t lds1 = (size_t)(2 * cap1 + a.E + 1) * 4;
+    const size_t lds1 = (size_t)(2 * cap1 + a.E + 1 + (a.K > 0 ? a.T * a.K : 0)) * 4;
     const size_t lds2 = (size_t)(2 * cap2 + a.E + 1) * 4;
     const hipError_t err = launch_u<DT, true>(unroll_gate_up(a.H), a, min(kStWgs1 * a.cus, max1), ns1, lds1, stream,
                                               marks ? marks[0] : Marks{});
