@@ -495,9 +495,14 @@ def main():
     outp, idxp, twp = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(tw.data_ptr())
     xp = ctypes.c_void_p(x.data_ptr())
 
-    def layer_call(c, xin, events=None):
+    def layer_call(c, xin, events=None, norm=None):
+        # norm: where the RMSNorm of this layer's output goes (the next layer's
+        # input), taken in the layer's combine (flint_moe_forward_rmsnorm)
         arr = None if events is None else (ctypes.c_void_p * 10)(*[e.value for e in events])
-        if wl.mx4:
+        if norm is not None:
+            st = lib.flint_moe_forward_rmsnorm(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, norm, 1e-6,
+                                               idxp, twp, wsp, wsn, sp, arr)
+        elif wl.mx4:
             st = lib.flint_moe_forward_mx4(dref, T, xin, ctypes.byref(wstructs[c]), outp, api.F32, idxp, twp,
                                            wsp, wsn, sp, arr)
         elif args.fused:
@@ -517,13 +522,9 @@ def main():
             return
         xin = xp
         for l in range(n_copies):
-            layer_call(l, xin, events[l] if events else None)
-            if l + 1 < n_copies:
-                nxt = xs[l % 2]
-                st = lib.flint_rmsnorm(T, wl.hidden, outp, ctypes.c_void_p(nxt.data_ptr()), 1e-6, sp)
-                if st != 0:
-                    raise api.FlintError(st, "flint_rmsnorm")
-                xin = ctypes.c_void_p(nxt.data_ptr())
+            nxt = ctypes.c_void_p(xs[l % 2].data_ptr()) if l + 1 < n_copies else None
+            layer_call(l, xin, events[l] if events else None, nxt)
+            xin = nxt
 
     # routing per copy (for the algorithmic byte counts)
     per_copy = []
@@ -538,13 +539,11 @@ def main():
         per_copy = []
         xin = xp
         for l in range(n_copies):
-            layer_call(l, xin)
+            nxt = ctypes.c_void_p(xs[l % 2].data_ptr()) if l + 1 < n_copies else None
+            layer_call(l, xin, None, nxt)
             torch.cuda.synchronize()
             per_copy.append(algorithmic(wl, idx.cpu().numpy()))
-            if l + 1 < n_copies:
-                nxt = xs[l % 2]
-                lib.flint_rmsnorm(T, wl.hidden, outp, ctypes.c_void_p(nxt.data_ptr()), 1e-6, sp)
-                xin = ctypes.c_void_p(nxt.data_ptr())
+            xin = nxt
 
     for i in range(args.warmup):
         step(i)

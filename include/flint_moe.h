@@ -297,6 +297,24 @@ flint_status flint_moe_forward_static(const flint_moe_dims *dims, int32_t T, con
 flint_status flint_rmsnorm(int32_t T, int32_t H, const float *in, void *out_bf16, float eps,
                            void *stream);
 
+/* The layer followed by that RMSNorm, for a stack of layers: flint_moe_forward_profiled
+ * (same arguments, workspace and results, and `out` as it writes it), and
+ * norm_out_bf16 [T][H] bf16 receives flint_rmsnorm(T, H, y, norm_out_bf16, eps)
+ * of the layer's float32 output y, bit for bit, whatever out_dtype is.  The
+ * norm runs inside the layer's last kernel, its combine (a work-group per
+ * token sums the row's squares in the order flint_rmsnorm does), so a stack
+ * makes one launch fewer per layer.  norm_out_bf16: device pointer, 16-byte
+ * aligned, caller-owned; it must not overlap out, and it may be x itself (x is
+ * not read after the expert products).  H must be a multiple of 64 and at most
+ * 8192, eps >= 0, else FLINT_UNSUPPORTED / FLINT_INVALID_ARG; a null
+ * norm_out_bf16 with T > 0 is FLINT_INVALID_ARG.  In `events` the combine
+ * stage covers the norm too. */
+flint_status flint_moe_forward_rmsnorm(const flint_moe_dims *dims, int32_t T, const void *x,
+                                       const flint_moe_weights *weights, void *out, flint_dtype out_dtype,
+                                       void *norm_out_bf16, float eps, int32_t *topk_idx_out,
+                                       float *topk_w_out, void *ws, size_t ws_bytes, void *stream,
+                                       void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,7 +46,7 @@ class DenseDims(ctypes.Structure):
 EXPORTS = ("flint_status_string", "flint_moe_workspace_bytes", "flint_moe_route", "flint_moe_dispatch",
            "flint_moe_forward", "flint_moe_forward_profiled", "flint_moe_forward_mx4",
            "flint_dense_workspace_bytes", "flint_dense_mlp", "flint_rmsnorm", "flint_moe_forward_static",
-           "flint_moe_forward_fused")
+           "flint_moe_forward_fused", "flint_moe_forward_rmsnorm")
 
 
 def load():
@@ -86,5 +86,8 @@ def load():
     lib.flint_moe_forward_static.restype = I32
     lib.flint_moe_forward_fused.argtypes = [D, I32, P, ctypes.POINTER(Weights), P, I32, P, P, P, SZ, P, P]
     lib.flint_moe_forward_fused.restype = I32
+    lib.flint_moe_forward_rmsnorm.argtypes = [D, I32, P, ctypes.POINTER(Weights), P, I32, P, ctypes.c_float, P, P,
+                                              P, SZ, P, P]
+    lib.flint_moe_forward_rmsnorm.restype = I32
     _lib = lib
     return lib

@@ -299,6 +299,34 @@ def dense_mlp(x, gate, up, down, out_dtype=torch.float32, ws=None, stream=None):
     return out
 
 
+def flint_moe_forward_rmsnorm(d: Dims, x, weights, out, norm_out, eps=1e-6, topk_idx_out=None, topk_w_out=None,
+                              ws=None, stream=None, events=None):
+    """The layer (as flint_moe_forward) and, in its combine, RMSNorm of its
+    float32 output into norm_out ([T][H] bfloat16; it may be x itself, not out);
+    events as in flint_moe_forward."""
+    T = x.shape[0]
+    _check_tensor("x", x, _elem(d), (T, d.hidden))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check_tensor("out", out, None, (T, d.hidden))
+    _check_tensor("norm_out", norm_out, torch.bfloat16, (T, d.hidden))
+    _check_tensor("topk_idx_out", topk_idx_out, torch.int32, (T, d.top_k))
+    _check_tensor("topk_w_out", topk_w_out, torch.float32, (T, d.top_k))
+    _check_tensor("ws", ws, torch.uint8)
+    ws_struct = weights if isinstance(weights, Weights) else weights_struct(d, weights)
+    out_dt = BF16 if out.dtype == torch.bfloat16 else F32
+    arr = None
+    if events is not None:
+        if len(events) != 10:
+            raise ValueError("events: 10 hipEvent_t handles (start/stop of 5 stages)")
+        arr = (ctypes.c_void_p * 10)(*[e.value if isinstance(e, ctypes.c_void_p) else e for e in events])
+    st = load().flint_moe_forward_rmsnorm(ctypes.byref(d), T, _ptr(x), ctypes.byref(ws_struct), _ptr(out), out_dt,
+                                          _ptr(norm_out), float(eps), _ptr(topk_idx_out), _ptr(topk_w_out),
+                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream), arr)
+    if st != OK:
+        raise FlintError(st, "flint_moe_forward_rmsnorm")
+
+
 def flint_rmsnorm(inp, out, eps=1e-6, stream=None):
     T, H = inp.shape
     _check_tensor("in", inp, torch.float32, (T, H))
@@ -327,6 +355,18 @@ def forward(d: Dims, x, weights, out_dtype=torch.float32, ws=None, stream=None, 
     else:
         flint_moe_forward(d, x, weights, out, idx, tw, ws, stream)
     return (out, idx, tw) if return_routing else out
+
+
+def forward_rmsnorm(d: Dims, x, weights, eps=1e-6, out_dtype=torch.float32, ws=None, stream=None):
+    """The layer and the RMSNorm of its float32 output (flint_moe_forward_rmsnorm):
+    returns (out, norm_out)."""
+    T = x.shape[0]
+    out = torch.empty((T, d.hidden), dtype=out_dtype, device=x.device)
+    norm = torch.empty((T, d.hidden), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = workspace(d, T, x.device)
+    flint_moe_forward_rmsnorm(d, x, weights, out, norm, eps, ws=ws, stream=stream)
+    return out, norm
 
 
 def route(d: Dims, x, router, bias=None, ws=None, stream=None):

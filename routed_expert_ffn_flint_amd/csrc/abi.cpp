@@ -491,6 +491,37 @@ flint_status flint_moe_forward_profiled(const flint_moe_dims *d, int32_t T, cons
                         stream, events);
 }
 
+flint_status flint_moe_forward_rmsnorm(const flint_moe_dims *d, int32_t T, const void *x,
+                                       const flint_moe_weights *wt, void *out, flint_dtype out_dtype,
+                                       void *norm_out_bf16, float eps, int32_t *topk_idx_out, float *topk_w_out,
+                                       void *ws, size_t ws_bytes, void *stream, void *const *events)
+{
+    flint_status st = check_forward(d, T, x, wt ? wt->router : nullptr, wt ? wt->router_bias : nullptr, out,
+                                    out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes);
+    if (st != FLINT_OK) return st;
+    if (d->hidden % 64 || d->hidden > 8192) return FLINT_UNSUPPORTED;
+    if (!(eps >= 0.0f)) return FLINT_INVALID_ARG;
+    if (T == 0) return FLINT_OK;
+    if (!norm_out_bf16) return FLINT_INVALID_ARG;
+    if (!aligned16(norm_out_bf16)) return FLINT_UNSUPPORTED;
+    const size_t row = (size_t)d->hidden, n_bytes = (size_t)T * row * 2,
+                 out_bytes = (size_t)T * row * (out_dtype == FLINT_BF16 ? 2 : 4);
+    const uintptr_t n0 = (uintptr_t)norm_out_bf16, o0 = (uintptr_t)out;
+    if (n0 < o0 + out_bytes && o0 < n0 + n_bytes) return FLINT_INVALID_ARG;  // overlaps out
+    if ((st = check_weights(d, wt)) != FLINT_OK) return st;
+    ExpertArgs e{};
+    e.gate = wt->gate;
+    e.up = wt->up;
+    e.down = wt->down;
+    e.shared_gate = wt->shared_gate;
+    e.shared_up = wt->shared_up;
+    e.shared_down = wt->shared_down;
+    e.norm_out = (uint16_t *)norm_out_bf16;
+    e.norm_eps = eps;
+    return launch_layer(d, T, x, wt->router, wt->router_bias, e, out, out_dtype, topk_idx_out, topk_w_out, ws,
+                        stream, events);
+}
+
 flint_status flint_moe_forward_fused(const flint_moe_dims *d, int32_t T, const void *x, const flint_moe_weights *wt,
                                      void *out, flint_dtype out_dtype, int32_t *topk_idx_out, float *topk_w_out,
                                      void *ws, size_t ws_bytes, void *stream, void *const *events)

@@ -228,13 +228,11 @@ __global__ __launch_bounds__(WaveGrid<SPLIT>::THREADS) void k_down(ExpertArgs a,
 // out[t] = sum_k w[t][k] * y_sorted[slot_of[t*K+k]] + y_shared[t]   (fixed order)
 // Y16: y_sorted and a single y_shared hold fp16 values times 2^y_scale (see
 // ExpertArgs::y16).
+// combine4: columns c .. c+3 of token t (c a multiple of 4, below H).
 template <bool Y16>
-__global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
+__device__ __forceinline__ f32x4 combine4(const ExpertArgs &a, int t, int c)
 {
-    const int t = blockIdx.x;
     const int H = a.H, K = a.K;
-    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
-    if (c >= H) return;
     // Every load is issued before any is used (entries past K re-read entry
     // K-1, rows past them are not added): the rows arrive in one memory
     // latency instead of one each.
@@ -307,15 +305,29 @@ __global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
         const float nan = __builtin_nanf("");
         acc = f32x4{nan, nan, nan, nan};
     }
+    return acc;
+}
+
+__device__ __forceinline__ void store_out4(const ExpertArgs &a, int t, int c, f32x4 acc)
+{
     if (a.out_bf16) {
-        uint16_t *o = (uint16_t *)a.out + (size_t)t * H + c;
+        uint16_t *o = (uint16_t *)a.out + (size_t)t * a.H + c;
         o[0] = f32_to_bf16(acc[0]);
         o[1] = f32_to_bf16(acc[1]);
         o[2] = f32_to_bf16(acc[2]);
         o[3] = f32_to_bf16(acc[3]);
     } else {
-        *reinterpret_cast<f32x4 *>((float *)a.out + (size_t)t * H + c) = acc;
+        *reinterpret_cast<f32x4 *>((float *)a.out + (size_t)t * a.H + c) = acc;
     }
+}
+
+template <bool Y16>
+__global__ __launch_bounds__(256) void k_combine(ExpertArgs a)
+{
+    const int t = blockIdx.x;
+    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+    if (c >= a.H) return;
+    store_out4(a, t, c, combine4<Y16>(a, t, c));
 }
 
 // ---------------------------------------------------------------------------
@@ -377,13 +389,6 @@ static hipError_t launch_experts_t(const ExpertArgs &a, hipStream_t stream, cons
     return a.skip_combine ? hipSuccess : launch_combine(a, stream, m3);
 }
 
-hipError_t launch_combine(const ExpertArgs &a, hipStream_t stream, Marks m)
-{
-    if (a.T <= 0) return hipSuccess;
-    const dim3 grid(a.T, (a.H + 1023) / 1024);
-    return a.y16 ? launch_k(k_combine<true>, grid, 256, 0, stream, m, a)
-                 : launch_k(k_combine<false>, grid, 256, 0, stream, m, a);
-}
 
 hipError_t launch_experts(const ExpertArgs &a, hipStream_t stream, const Marks *marks)
 {
@@ -408,21 +413,61 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double d)
     return f32_to_bf16(f);
 }
 
-__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ in, int H, float eps,
-                                                 uint16_t *__restrict__ out)
+// One row by a work-group of 256 threads (row in global memory or LDS): the
+// sum of squares in the same order wherever the row lies, so the result has
+// the same bits.  part: 4 doubles of LDS.
+__device__ __forceinline__ void rmsnorm_row(const float *row, int H, float eps, uint16_t *__restrict__ out,
+                                            double *part)
 {
-    __shared__ double part[4];
-    const int t = blockIdx.x;
-    const float *row = in + (size_t)t * H;
     double ss = 0.0;
-    for (int c = threadIdx.x; c < H; c += blockDim.x) ss += (double)row[c] * (double)row[c];
+    for (int c = threadIdx.x; c < H; c += 256) ss += (double)row[c] * (double)row[c];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
     __syncthreads();
     const double tot = part[0] + part[1] + part[2] + part[3];
     const double r = 1.0 / sqrt(tot / (double)H + (double)eps);
-    for (int c = threadIdx.x; c < H; c += blockDim.x) out[(size_t)t * H + c] = f64_to_bf16((double)row[c] * r);
+    for (int c = threadIdx.x; c < H; c += 256) out[c] = f64_to_bf16((double)row[c] * r);
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ in, int H, float eps,
+                                                 uint16_t *__restrict__ out)
+{
+    __shared__ double part[4];
+    const int t = blockIdx.x;
+    rmsnorm_row(in + (size_t)t * H, H, eps, out + (size_t)t * H, part);
+}
+
+// The combine of one token row, then RMSNorm of its float32 sums into
+// a.norm_out, in one work-group: the row goes through LDS (H floats of
+// dynamic LDS), where the norm reads it in k_rmsnorm's order, so the bits are
+// those of k_rmsnorm on the float32 output.
+template <bool Y16>
+__global__ __launch_bounds__(256) void k_combine_rmsnorm(ExpertArgs a)
+{
+    extern __shared__ float row[];
+    __shared__ double part[4];
+    const int t = blockIdx.x;
+    for (int c = threadIdx.x * 4; c < a.H; c += 256 * 4) {
+        const f32x4 acc = combine4<Y16>(a, t, c);
+        store_out4(a, t, c, acc);
+        *reinterpret_cast<f32x4 *>(row + c) = acc;
+    }
+    __syncthreads();
+    rmsnorm_row(row, a.H, a.norm_eps, a.norm_out + (size_t)t * a.H, part);
+}
+
+hipError_t launch_combine(const ExpertArgs &a, hipStream_t stream, Marks m)
+{
+    if (a.T <= 0) return hipSuccess;
+    if (a.norm_out) {
+        const size_t lds = (size_t)a.H * 4;
+        return a.y16 ? launch_k(k_combine_rmsnorm<true>, a.T, 256, lds, stream, m, a)
+                     : launch_k(k_combine_rmsnorm<false>, a.T, 256, lds, stream, m, a);
+    }
+    const dim3 grid(a.T, (a.H + 1023) / 1024);
+    return a.y16 ? launch_k(k_combine<true>, grid, 256, 0, stream, m, a)
+                 : launch_k(k_combine<false>, grid, 256, 0, stream, m, a);
 }
 
 hipError_t launch_rmsnorm(int T, int H, const float *in, uint16_t *out, float eps, hipStream_t stream)

@@ -186,6 +186,10 @@ struct ExpertArgs {
     int shared_splits;
     void *out;
     bool out_bf16;
+    // Non-null: the combine also writes RMSNorm of each float32 output row
+    // (epsilon norm_eps) to norm_out, [T][H] bf16.
+    uint16_t *norm_out;
+    float norm_eps;
     bool skip_combine;  // the shared down stage writes the output itself (a dense layer, float32 out)
     ExpertTiles tiles;
     int cus;  // compute units of the device (sizes the persistent kernels' grids)

@@ -255,3 +255,26 @@ def test_forward_fused_refusals(lib):
     assert call(flint_dims(hidden=128), 32) == api.UNSUPPORTED
     assert call(flint_dims(inter=192, shared_inter=0), 32) == api.UNSUPPORTED
     assert call(flint_dims(shared_inter=768), 32) == api.UNSUPPORTED  # not a multiple of I = 512
+
+
+def test_forward_rmsnorm_refusals(lib):
+    """flint_moe_forward_rmsnorm makes flint_moe_forward's checks, then its own:
+    a norm output that is given, 16-byte aligned and clear of out, and eps >= 0."""
+    d = flint_dims()
+    need = api.flint_moe_workspace_bytes(d, 32)
+    w = _lib.Weights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    norm_ok = 0x200000  # clear of out (32 x 2048 float32 from FAKE) and of the workspace
+
+    def call(T, norm=norm_ok, eps=1e-6, ws_bytes=need, out=FAKE):
+        return lib.flint_moe_forward_rmsnorm(ctypes.byref(d), T, FAKE, ctypes.byref(w), out, api.F32, norm, eps,
+                                             None, None, FAKE_WS, ws_bytes, None, None)
+    assert call(-1) == api.INVALID_ARG
+    assert call(0, norm=None) == api.OK  # no-op, nothing launched
+    assert call(32, out=None) == api.INVALID_ARG
+    assert call(32, norm=None) == api.INVALID_ARG
+    assert call(32, norm=norm_ok + 8) == api.UNSUPPORTED  # misaligned
+    assert call(32, eps=-1.0) == api.INVALID_ARG
+    assert call(32, eps=float("nan")) == api.INVALID_ARG
+    assert call(32, ws_bytes=need - 1) == api.WORKSPACE_TOO_SMALL
+    assert call(32, norm=FAKE + 0x10000) == api.INVALID_ARG  # inside out
+    assert call(32, norm=FAKE - 0x10000 + 16) == api.INVALID_ARG  # runs into out

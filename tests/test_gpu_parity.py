@@ -460,6 +460,41 @@ def test_empty_batch_is_a_noop():
     assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
 
 
+@pytest.mark.parametrize("shape", [
+    ("fr1", 1, 2048, 256, 6, 512, 1024, True),     # streaming kernels
+    ("fr32", 32, 2048, 256, 6, 512, 1024, True),   # streaming kernels
+    ("fr200", 200, 2048, 256, 6, 512, 1024, True),  # 16-row tiles
+    ("fr600", 600, 2048, 256, 6, 512, 1024, True),  # large tiles (fp16 routed outputs)
+    ("fr64_f32", 64, 256, 16, 2, 256, 512, False),  # float32 layer
+], ids=lambda s: s[0])
+def test_forward_rmsnorm_equals_forward_then_rmsnorm(shape):
+    """flint_moe_forward_rmsnorm gives flint_moe_forward's output and, as its
+    norm, flint_rmsnorm of the float32 output, bit for bit, on every kernel path;
+    with a bf16 out too, and with the norm written over x."""
+    name, T, H, E, K, I, Is, bf16 = shape
+    wl = inputs.custom(name, T, H, E, K, I, Is, bf16, seed=9)
+    w, x = _layer(wl)
+    d = api.dims_of(wl)
+    eps = 1e-6
+    ref = api.forward(d, x, w)
+    ref_norm = api.rmsnorm(ref, eps)
+    out, norm = api.forward_rmsnorm(d, x, w, eps)
+    ref16 = api.forward(d, x, w, out_dtype=torch.bfloat16)
+    out16, norm16 = api.forward_rmsnorm(d, x, w, eps, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), f"{name}: layer output differs"
+    assert torch.equal(norm.view(torch.uint8), ref_norm.view(torch.uint8)), f"{name}: norm differs"
+    assert torch.equal(out16.view(torch.uint8), ref16.view(torch.uint8)), f"{name}: bf16 layer output differs"
+    assert torch.equal(norm16.view(torch.uint8), ref_norm.view(torch.uint8)), f"{name}: norm (bf16 out) differs"
+    if bf16:  # the next layer's input written over this layer's
+        xx = x.clone()
+        out2 = torch.empty_like(ref)
+        api.flint_moe_forward_rmsnorm(d, xx, w, out2, xx, eps, ws=api.workspace(d, T, x.device))
+        torch.cuda.synchronize()
+        assert torch.equal(xx.view(torch.uint8), ref_norm.view(torch.uint8)), f"{name}: norm over x differs"
+        assert torch.equal(out2.view(torch.uint8), ref.view(torch.uint8)), f"{name}: output with the norm over x"
+
+
 def test_rmsnorm_matches_oracle():
     y = torch.randn((300, 2048), generator=torch.Generator().manual_seed(5)) * 3
     eps = float(np.float32(1e-6))
