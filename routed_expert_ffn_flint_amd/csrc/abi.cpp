@@ -132,6 +132,7 @@ static Workspace plan_workspace_out(void *base, const void *out, int T, int H, i
     phase();
     w.y_shared = (float *)take((size_t)shared_splits * T * H * 4);
     if (tiles.tiled && K > 0) w.y_scale = (int8_t *)take((TK + T) * (H / kYScaleCols));
+    if (K > 0 && T <= kTopkTile) w.done = (int32_t *)take(4);
     if (eb == 2 && K > 0 && T <= kFusedMaxT) {  // the fused decode kernel's own state
         w.topk_q = (int32_t *)take((size_t)kFusedQueues * TK * 4);
         w.sync = (int32_t *)take((size_t)kFusedSyncWords * 4);
@@ -323,8 +324,10 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
         for (int i = 0; i < 5; ++i) marks[i] = Marks{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]};
     const ExpertTiles tiles = expert_tiles_for(T, d->hidden, d->n_experts, d->top_k, d->inter, d->shared_inter,
                                                d->dtype == FLINT_BF16);
+    // the router kernel also zeroes the counters of what follows it: the fused
+    // decode kernel's, or that of the one-tile top-k + dispatch
     if (launch_router_logits(bf16, x, T, d->hidden, router, router_bias, d->n_experts, w.logits, s, marks[0],
-                             fused ? w.sync : nullptr, fused ? kFusedSyncWords : 0) != hipSuccess)
+                             fused ? w.sync : w.done, fused ? kFusedSyncWords : (w.done ? 1 : 0)) != hipSuccess)
         return FLINT_DEVICE_ERROR;
     if (fused) {
         // top-k, dispatch, gate/up and down in one launch (stage marks: the
@@ -382,6 +385,7 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
     a.offsets = w.offsets;
     a.sorted_token = w.sorted_token;
     a.slot_of = w.slot_of;
+    a.done = w.done;  // zeroed by the router kernel above
     if (launch_topk_dispatch(a, s, marks[1]) != hipSuccess) return FLINT_DEVICE_ERROR;
 
     e.bf16 = bf16;

@@ -104,14 +104,6 @@ __device__ __forceinline__ void wave_wait_ge(const int32_t *p, int target, int32
     }
 }
 
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, the other counters at their "no wait" maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 struct FusedLds {
     // split-k sums of one item: read and written 16 bytes a lane, so 16-byte

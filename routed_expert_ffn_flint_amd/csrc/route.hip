@@ -22,6 +22,9 @@
 //                    kernels' tile lists.
 //   k_topk_dispatch_small  up to 16 tokens: the top-k of k_topk_wave and the
 //                    one-tile dispatch in a single work-group
+//   k_topk_dispatch_last  17 to 128 tokens in a layer call: the top-k of
+//                    k_topk_wave, and the one-tile dispatch in the work-group
+//                    that finishes last
 //   k_dispatch_scan  (more than one tile) column scan of the tile histograms,
 //                    expert offsets, tile lists.
 //   k_dispatch_scatter (more than one tile) slot = offset + tile base + rank.
@@ -32,6 +35,12 @@ constexpr int kTopkWaveT = 4096;  // largest batch selected one token per wave (
 // one token per wave (T = 8: 10.2 -> 7.4 us; with two tokens per wave their
 // latencies add up: T = 32 9.8 -> 12.9 us).
 constexpr int kTopkFusedT = 16;
+// Largest batch of a layer call whose top-k and dispatch run as one launch of
+// many work-groups, the dispatch in the last one (k_topk_dispatch_last; top-k
+// + dispatch T = 32 10.0 -> 8.3 us, T = 128 10.5 -> 9.5; at T = 256 one
+// work-group of 256 threads dispatching 1536 pairs was slower than the
+// 1024-thread dispatch kernel, 12.5 -> 12.9 us).
+constexpr int kTopkLastMaxT = 128;
 
 #include "gemm_core.hpp"
 #include "launch.hpp"
@@ -336,8 +345,11 @@ struct TileLds {
 // the tile's per-expert histogram.  When the whole batch is one tile
 // (`single`) the same work-group also scans the counts, scatters the
 // permutation and writes the expert kernels' tile lists.
+// coherent: read the selection with agent-coherent loads (other work-groups of
+// the same launch wrote it).
 template <int NT>
-__device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, TileLds &L, bool sel_in_lds)
+__device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, TileLds &L, bool sel_in_lds,
+                              bool coherent = false)
 {
     constexpr int PER = kTopkTile * kMaxTopK / NT;  // pairs per thread, at most
     constexpr int W = kTopkTile / 32;
@@ -346,7 +358,10 @@ __device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, Tile
     const int tile_len = min(kTopkTile, a.T - t_base);
 
     if (!sel_in_lds)
-        for (int i = threadIdx.x; i < tile_len * K; i += NT) L.sel[i] = (int16_t)a.topk_idx[(size_t)t_base * K + i];
+        for (int i = threadIdx.x; i < tile_len * K; i += NT) {
+            const int32_t *p = a.topk_idx + (size_t)t_base * K + i;
+            L.sel[i] = (int16_t)(coherent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p);
+        }
     for (int i = threadIdx.x; i < E * W; i += NT) L.masks[i] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < tile_len * K; i += NT) {
@@ -510,6 +525,40 @@ __global__ __launch_bounds__(1024) void k_topk_dispatch_small(DispatchArgs a)
     dispatch_tile<1024>(a, 0, true, L, true);
 }
 
+// 17 to kTopkLastMaxT tokens (one tile): the top-k of k_topk_wave (one token
+// per wave, four per work-group), and the dispatch in the work-group that
+// finishes its tokens last, counted on a.done (zeroed by the router kernel
+// before): one launch instead of two.  The selection crosses work-groups through
+// agent-coherent stores, acknowledged (vmcnt 0) before the counter is raised,
+// and agent-coherent loads in the last work-group; no work-group waits for
+// another.
+__global__ __launch_bounds__(256) void k_topk_dispatch_last(DispatchArgs a)
+{
+    __shared__ TileLds L;
+    __shared__ float ls[4][kMaxTopK];
+    __shared__ int le[4][kMaxTopK];
+    __shared__ int is_last;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t < a.T) {
+        int idx;
+        float w;
+        wave_topk_select(a.logits + (size_t)t * a.E, (size_t)a.T * a.E, a.logit_splits, a.E, a.K, ls[wave],
+                         le[wave], idx, w);
+        if (lane < a.K) {
+            __hip_atomic_store(a.topk_idx + (size_t)t * a.K + lane, idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a.topk_w[(size_t)t * a.K + lane] = w;
+        }
+    }
+    wait_vmcnt<0>();  // this wave's stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0)
+        is_last = __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!is_last) return;
+    dispatch_tile<256>(a, 0, true, L, false, true);
+}
+
 // More than one tile: per-expert column scan of the tile histograms.
 __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a, int ntiles)
 {
@@ -572,6 +621,8 @@ hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks
     hipError_t err = hipSuccess;
     if (a.compute_topk && a.dispatch && fused && a.T <= kTopkFusedT && a.E <= 256)
         return launch_k(k_topk_dispatch_small, 1, 1024, 0, stream, m, a);
+    if (a.compute_topk && a.dispatch && fused && a.done && a.T <= kTopkLastMaxT && a.E <= 256)
+        return launch_k(k_topk_dispatch_last, (a.T + 3) / 4, 256, 0, stream, m, a);
     if (a.compute_topk) {
         err = a.T <= kTopkWaveT ? launch_k(k_topk_wave, (a.T + 3) / 4, 256, 0, stream, first, a)
                           : launch_k(k_topk<16>, (a.T + 15) / 16, 256, 0, stream, first, a);

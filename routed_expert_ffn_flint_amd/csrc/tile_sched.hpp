@@ -44,14 +44,6 @@ __device__ __forceinline__ int xcd_item2(int ns, int nr)
     return (s2 < pr && r < nr) ? ns + r : -1;
 }
 
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others at their "no wait" maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 // s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
