@@ -127,11 +127,12 @@ __global__ __launch_bounds__(SPLIT > 1 ? SPLIT * 64 : 256) void k_router_logits(
         }
 }
 
-// Below 128 tiles of 16 tokens x 16 experts (T = 32, E = 256: 32 tiles) each
+// Up to 128 tiles of 16 tokens x 16 experts (T = 32, E = 256: 32 tiles) each
 // tile's sum over H is split between two work-groups of 8 waves, each writing
 // its own partial array (top-k adds the two in order), so twice as many CUs
-// read the router matrix: measured 5.8 -> 4.2 us at T = 32 (four or eight
-// partial arrays cost top-k more than they save).
+// read the router matrix: measured 5.8 -> 4.2 us at T = 32 and 6.1 -> 4.3 us at
+// T = 128 (four or eight partial arrays cost top-k more than they save; at 256
+// tiles, T = 256, the split gained nothing, 6.1 -> 6.0 us).
 constexpr int kRouterSmallSplits = 2;
 static_assert(kRouterSmallSplits == 1 || kRouterSmallSplits == 2 || kRouterSmallSplits == 4 ||
                   kRouterSmallSplits == 8,
@@ -140,7 +141,7 @@ int small_router_splits(int T, int H, int E)
 {
     const long long tiles = (long long)((E + 15) / 16) * ((T + 15) / 16);
     const int s = kRouterSmallSplits;
-    return s > 1 && tiles < 128 && H % (32 * s) == 0 ? s : 1;
+    return s > 1 && tiles <= 128 && H % (32 * s) == 0 ? s : 1;
 }
 
 hipError_t launch_router_logits(bool bf16, const void *x, int T, int H, const void *router,
