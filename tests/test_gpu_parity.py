@@ -56,6 +56,9 @@ SMALL = [
     ("t24_e256_k8", 24, 2048, 256, 8, 512, 1024, True, True),  # the most experts and the largest K
     ("t64_k1",    64, 128, 16, 1, 128, 64,  True,  True),
     ("t100_f32",  100, 128, 24, 4, 64, 128, False, True),
+    # the largest batch whose top-k and dispatch run as one launch, and the next
+    ("t128_flint", 128, 2048, 256, 6, 512, 1024, True, False),
+    ("t129",      129, 256, 64, 6, 128, 128, True, True),
     ("t300",      300, 256, 64, 6, 128, 128, True, False),   # two dispatch tiles, 16-row tiles
     ("t600_f32",  600, 128, 16, 2, 64, 64,  False, False),
     ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
