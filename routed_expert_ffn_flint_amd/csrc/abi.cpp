@@ -132,7 +132,7 @@ static Workspace plan_workspace_out(void *base, const void *out, int T, int H, i
     phase();
     w.y_shared = (float *)take((size_t)shared_splits * T * H * 4);
     if (tiles.tiled && K > 0) w.y_scale = (int8_t *)take((TK + T) * (H / kYScaleCols));
-    if (K > 0 && T <= kTopkTile) w.done = (int32_t *)take(4);
+    if (K > 0) w.done = (int32_t *)take(4);
     if (eb == 2 && K > 0 && T <= kFusedMaxT) {  // the fused decode kernel's own state
         w.topk_q = (int32_t *)take((size_t)kFusedQueues * TK * 4);
         w.sync = (int32_t *)take((size_t)kFusedSyncWords * 4);
@@ -326,8 +326,9 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
                                                d->dtype == FLINT_BF16);
     // the router kernel also zeroes the counters of what follows it: the fused
     // decode kernel's, or that of the one-tile top-k + dispatch
-    if (launch_router_logits(bf16, x, T, d->hidden, router, router_bias, d->n_experts, w.logits, s, marks[0],
-                             fused ? w.sync : w.done, fused ? kFusedSyncWords : (w.done ? 1 : 0)) != hipSuccess)
+    int32_t *const zero = fused ? w.sync : (T <= kTopkTile ? w.done : nullptr);
+    if (launch_router_logits(bf16, x, T, d->hidden, router, router_bias, d->n_experts, w.logits, s, marks[0], zero,
+                             fused ? kFusedSyncWords : (zero ? 1 : 0)) != hipSuccess)
         return FLINT_DEVICE_ERROR;
     if (fused) {
         // top-k, dispatch, gate/up and down in one launch (stage marks: the
@@ -385,7 +386,7 @@ static flint_status launch_layer(const flint_moe_dims *d, int32_t T, const void 
     a.offsets = w.offsets;
     a.sorted_token = w.sorted_token;
     a.slot_of = w.slot_of;
-    a.done = w.done;  // zeroed by the router kernel above
+    a.done = w.done;  // one tile: zeroed by the router kernel above; several: by the top-k kernel
     if (launch_topk_dispatch(a, s, marks[1]) != hipSuccess) return FLINT_DEVICE_ERROR;
 
     e.bf16 = bf16;

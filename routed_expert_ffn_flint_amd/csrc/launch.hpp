@@ -106,7 +106,7 @@ struct Workspace {
     int8_t *y_scale;      // [T*K + T][H/64]: power-of-two exponents of fp16 y_sorted, then of fp16 y_shared
     int32_t *topk_q;      // fused decode: [queues][T][K] per-queue copies of the selection
     int32_t *sync;        // fused decode: kFusedSyncWords counters
-    int32_t *done;        // [1] one-tile top-k + dispatch: work-groups finished (DispatchArgs::done)
+    int32_t *done;        // [1] top-k / dispatch work-groups finished (DispatchArgs::done)
     size_t bytes;         // total bytes needed
 };
 
@@ -157,10 +157,12 @@ struct DispatchArgs {
     // null: none)
     int8_t *y_scale;
     int scale_cols;
-    // Non-null (compute_topk and dispatch of a one-tile batch): a counter that
-    // is 0 when the launch starts; batches of 17 to 128 tokens then run the
-    // top-k and the dispatch as one launch, the dispatch in the work-group that
-    // finishes its tokens last.
+    // Non-null (compute_topk and dispatch): a counter word in the workspace.
+    // A one-tile batch finds it at 0 (the router kernel clears it) and, from 17
+    // to 128 tokens, runs the top-k and the dispatch as one launch, the
+    // dispatch in the work-group that finishes its tokens last.  With several
+    // tiles the top-k kernel clears it, and the tile work-group that finishes
+    // last also scans the tile histograms (no separate scan launch).
     int32_t *done;
 };
 hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks m = {});

@@ -26,7 +26,8 @@
 //                    k_topk_wave, and the one-tile dispatch in the work-group
 //                    that finishes last
 //   k_dispatch_scan  (more than one tile) column scan of the tile histograms,
-//                    expert offsets, tile lists.
+//                    expert offsets, tile lists (in a layer call the last
+//                    k_dispatch_tile work-group does this instead).
 //   k_dispatch_scatter (more than one tile) slot = offset + tile base + rank.
 #include <climits>
 
@@ -395,7 +396,13 @@ __device__ void dispatch_tile(const DispatchArgs &a, int tile, bool single, Tile
             const int i = threadIdx.x + r * NT;
             if (my_e[r] >= 0) a.rank[(size_t)t_base * K + i] = my_rank[r];
         }
-        if (threadIdx.x < E) a.hist[(size_t)tile * E + threadIdx.x] = hcount;
+        if (threadIdx.x < E) {
+            int32_t *h = a.hist + (size_t)tile * E + threadIdx.x;
+            if (a.done)  // the last tile's work-group reads it in this launch
+                __hip_atomic_store(h, hcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                *h = hcount;
+        }
         return;
     }
     const int off = finish_offsets_and_lists(hcount, E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2,
@@ -482,6 +489,8 @@ __global__ __launch_bounds__(256) void k_topk_wave(DispatchArgs da)
     __shared__ int le[4][kMaxTopK];
     const int wave = threadIdx.x >> 6;
     const int tok = blockIdx.x * 4 + wave;
+    if (da.done && da.dispatch && da.T > kTopkTile && blockIdx.x == 0 && threadIdx.x == 0)
+        *da.done = 0;  // for the dispatch kernels that follow (several tiles)
     if (tok >= da.T) return;  // whole waves
     wave_topk(da.logits + (size_t)tok * da.E, (size_t)da.T * da.E, da.logit_splits, da.E, da.K, tok, da.topk_idx,
               da.topk_w, ls[wave], le[wave]);
@@ -498,15 +507,31 @@ __global__ __launch_bounds__(256) void k_topk(DispatchArgs da)
     const int tok = blockIdx.x * groups_per_block + threadIdx.x / G;
     const int gl = threadIdx.x & (G - 1);
     const int t = tok < T ? tok : T - 1;  // whole groups share a token; extra groups redo the last one
+    if (da.done && da.dispatch && T > kTopkTile && blockIdx.x == 0 && threadIdx.x == 0)
+        *da.done = 0;  // for the dispatch kernels that follow (several tiles)
     uint64_t l[kMaxTopK];
     group_top8<G>(logits + (size_t)t * E, (size_t)T * E, da.logit_splits, E, l);
     if (tok < T) write_topk(l, t, K, gl, topk_idx, topk_w);
 }
 
+__device__ void scan_tiles(const DispatchArgs &a, int ntiles, int *lds, bool coherent);
+
+// Several tiles with a.done: the work-group that finishes its tile last (its
+// histogram stores acknowledged first, like every other's) also scans the
+// histograms, in place of k_dispatch_scan.
 __global__ __launch_bounds__(1024) void k_dispatch_tile(DispatchArgs a, int fused_single_tile)
 {
     __shared__ TileLds L;
+    __shared__ int is_last;
     dispatch_tile<1024>(a, blockIdx.x, fused_single_tile != 0, L, false);
+    if (fused_single_tile || !a.done) return;
+    wait_vmcnt<0>();  // this wave's histogram stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0)
+        is_last = __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!is_last) return;
+    scan_tiles(a, gridDim.x, L.lds, true);
 }
 
 // Small batches (up to 16 tokens): top-k (one token per wave, 16 waves) and
@@ -561,16 +586,23 @@ __global__ __launch_bounds__(256) void k_topk_dispatch_last(DispatchArgs a)
 }
 
 // More than one tile: per-expert column scan of the tile histograms.
-__global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a, int ntiles)
+// Thread e < E scans expert e's column of the tile histograms (coherent: with
+// agent-coherent loads, the histograms written by other work-groups of the
+// same launch); then the offsets and the tile lists.  Every thread of the
+// work-group (at least 256) calls it; lds holds 12 ints.
+__device__ void scan_tiles(const DispatchArgs &a, int ntiles, int *lds, bool coherent)
 {
-    __shared__ int lds[12];
     const int e = threadIdx.x;
     int run = 0;
     if (e < a.E) {
         for (int tile = 0; tile < ntiles; tile += 8) {
             int h[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) h[j] = tile + j < ntiles ? a.hist[(size_t)(tile + j) * a.E + e] : 0;
+            for (int j = 0; j < 8; ++j) {
+                const int32_t *p = a.hist + (size_t)(tile + j < ntiles ? tile + j : 0) * a.E + e;
+                const int v = coherent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+                h[j] = tile + j < ntiles ? v : 0;
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if (tile + j < ntiles) a.tile_base[(size_t)(tile + j) * a.E + e] = run;
@@ -580,6 +612,12 @@ __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a, int ntile
     }
     finish_offsets_and_lists(run, a.E, a.offsets, a.counts, a.list1, a.bm1, a.list2, a.bm2,
                              a.meta, lds);
+}
+
+__global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a, int ntiles)
+{
+    __shared__ int lds[12];
+    scan_tiles(a, ntiles, lds, false);
 }
 
 __global__ __launch_bounds__(256) void k_dispatch_scatter(DispatchArgs a)
@@ -631,12 +669,18 @@ hipError_t launch_topk_dispatch(const DispatchArgs &a, hipStream_t stream, Marks
         first.start = nullptr;
     }
     if (a.dispatch) {
-        err = launch_k(k_dispatch_tile, ntiles, 1024, 0, stream, Marks{first.start, fused ? m.stop : nullptr}, a,
+        // several tiles: the last tile work-group scans the histograms when the
+        // top-k kernel above has cleared the counter; else k_dispatch_scan does
+        DispatchArgs b = a;
+        if (!a.compute_topk) b.done = nullptr;
+        err = launch_k(k_dispatch_tile, ntiles, 1024, 0, stream, Marks{first.start, fused ? m.stop : nullptr}, b,
                        fused);
         if (err != hipSuccess || fused) return err;
-        err = launch_k(k_dispatch_scan, 1, 256, 0, stream, Marks{}, a, ntiles);
-        if (err != hipSuccess) return err;
-        err = launch_k(k_dispatch_scatter, (a.T * a.K + 255) / 256, 256, 0, stream, Marks{nullptr, m.stop}, a);
+        if (!b.done) {
+            err = launch_k(k_dispatch_scan, 1, 256, 0, stream, Marks{}, b, ntiles);
+            if (err != hipSuccess) return err;
+        }
+        err = launch_k(k_dispatch_scatter, (a.T * a.K + 255) / 256, 256, 0, stream, Marks{nullptr, m.stop}, b);
     }
     return err;
 }
