@@ -732,13 +732,15 @@ def test_mx4_scale_extremes_and_nan_blocks():
 
 GRAPH_CASES = [
     # workload,       T
-    ("decode32",      8),     # one-launch top-k + dispatch, streaming experts
-    ("decode32",      32),    # the decode batch
+    ("decode32",      8),     # one-work-group top-k + dispatch, streaming experts
+    ("decode32",      32),    # the decode batch: top-k + dispatch in one launch of many work-groups
     ("decode32",      200),   # one-work-group dispatch, 16-row tiles
     ("prefill4096",   600),   # three-kernel dispatch, tiled experts
     ("decode32_mx4",  32),    # MXFP4 expert weights
     ("dense32",       32),    # dense layer, 32-row tiles, split down product
     ("dense4096",     600),   # dense layer, tiled, split down product
+    ("stack47",       256),   # flint_moe_forward_rmsnorm: the norm in the combine
+    ("stack47",       64),    # the same on the streaming kernels
 ]
 
 
@@ -777,9 +779,16 @@ def test_graph_replays_match_eager(case):
         else:
             wst = api.weights_struct(d, w)
             entry = api.flint_moe_forward
+        stacked = wl.layers > 1
+        if stacked:  # the layer with the norm of its output (the next layer's input)
+            refs.append(api.rmsnorm(refs[0]))
+            outs.append(torch.empty_like(refs[3]))
 
         def call():
-            entry(d, x, wst, outs[0], outs[1], outs[2], ws)
+            if stacked:
+                api.flint_moe_forward_rmsnorm(d, x, wst, outs[0], outs[3], 1e-6, outs[1], outs[2], ws)
+            else:
+                entry(d, x, wst, outs[0], outs[1], outs[2], ws)
 
         def dirty():
             api.forward(d, x2, w, ws=ws)
