@@ -90,6 +90,15 @@ using CfgWide = Cfg<256, 128, 128, 64, 32, 6>;  // 4 waves
 using CfgBig = Cfg<256, 256, 128, 128, 32, 4>;  // 4 waves
 using CfgBig8 = Cfg<256, 256, 128, 64, 32, 4>;  // 8 waves
 using CfgWideN = Cfg<128, 256, 64, 64, 64, 3>;  // 8 waves
+// A routed layer of a few dozen rows per expert: 64-row tiles in 4 stages (the
+// whole LDS), so less of each tile is padding and more of the weights are in
+// flight per CU.  Layer times on the Flint shape (H = 2048, 256 experts, top 6,
+// widths 512 / 1024) against the 128 x 256 tiles: T = 640 374 -> 363 us,
+// 1024 387 -> 375 (gate/up and down on 64-row tiles), 1536 407 -> 396 (gate/up
+// only); slower from 48 rows per expert (T = 2048: gate/up 230 -> 244 us, down
+// on them from 36 rows: 127 -> 132).  CfgMidN: widths not whole 128-channel tiles.
+using CfgMid = Cfg<64, 256, 32, 64, 64, 4>;   // 8 waves
+using CfgMidN = Cfg<64, 128, 32, 64, 64, 4>;  // 4 waves
 // The router from T = 1024 on: 64 tokens x all 256 experts, so each token row
 // is read from HBM once and the 1 MiB router matrix (read by every row tile)
 // from L2 (T = 1024 16.7 -> 12.7 us, 4096 19.3 -> 15.1, 16384 39.9 -> 35.6
@@ -534,18 +543,22 @@ __global__ __launch_bounds__(C::THREADS, C::WGS_PER_CU) void k_tiled(TiledArgs t
 // Host side
 
 constexpr int kTlBigRows = 256;  // mean rows per expert from which the down product takes 256 x 256 tiles
-// Gate/up on 128 x 256 tiles (a routed layer at every size; a dense layer
+// Gate/up on 128 x 256 tiles (a routed layer above kTlMidGuRows rows per expert; a dense layer
 // unless its 256 x 256 tiles come in fewer waves, see dense_gu_big) (which: 0 CfgSmall, 1 CfgWide,
 // 2 CfgBig, 3 CfgBig8, 6 CfgWideN; T = 4096: 290 -> 280 us against CfgSmall;
 // T = 16384: 667 -> 625 us against CfgBig8, 879 with CfgBig, 946 with CfgWide).
 constexpr int kTlGuWide = 6;
 constexpr int kTlDnSmall = 6;  // (T = 2048: 128 x 256 tiles 154 -> 144 us; even at 4096)
 constexpr int kTlDnBig = 3;  // (T = 16384: 8 waves measured 3% faster for the layer than 4; 128 x 256: 498 vs 478 us)
+// mean rows per expert (T K / E) up to which gate/up (down) takes the 64-row tiles
+constexpr int kTlMidGuRows = 40;
+constexpr int kTlMidDnRows = 24;
+constexpr int kTlMid = 7;
 
 namespace {
 
-// which: 0 CfgSmall, 1 CfgWide, 2 CfgBig, 3 CfgBig8, 6 CfgWideN
-int cfg_bm(int which) { return which >= 1 && which <= 3 ? 256 : 128; }
+// which: 0 CfgSmall, 1 CfgWide, 2 CfgBig, 3 CfgBig8, 6 CfgWideN, 7 CfgMid
+int cfg_bm(int which) { return which == kTlMid ? 64 : which >= 1 && which <= 3 ? 256 : 128; }
 int cfg_bn(int which) { return which >= 2 ? 256 : 128; }
 
 bool big_batch(int T, int K, int E) { return (long long)T * K >= (long long)kTlBigRows * E; }
@@ -568,11 +581,12 @@ bool dense_gu_big(int T, int Is)
 int gu_cfg(int T, int K, int E, int Is)
 {
     if (K == 0) return Is % 128 == 0 && dense_gu_big(T, Is) ? 3 : kTlGuWide;
-    return kTlGuWide;
+    return (long long)T * K <= (long long)kTlMidGuRows * E ? kTlMid : kTlGuWide;
 }
 int dn_cfg(int T, int K, int E)
 {
     if (K == 0) return 3;
+    if ((long long)T * K <= (long long)kTlMidDnRows * E) return kTlMid;
     return big_batch(T, K, E) ? kTlDnBig : kTlDnSmall;
 }
 // the 16-row tiles of a MoE layer and the 32-row tiles of a dense layer
@@ -608,6 +622,11 @@ hipError_t launch_mode(int which, const TiledArgs &ta, hipStream_t stream, Marks
         // 128 x 256 tiles (128 gate + 128 up channels): whole tiles of the widths, else 128 x 128
         if (MODE != GATE_UP || (ta.e.I % 128 == 0 && ta.e.Is % 128 == 0)) return launch_cfg<MODE, CfgWideN>(ta, stream, m);
         return launch_cfg<MODE, CfgSmall>(ta, stream, m);
+    case kTlMid:
+        // 64 x 256 tiles (128 gate + 128 up channels): whole tiles of the widths, else 64 x 128
+        if constexpr (MODE == GATE_UP)
+            if (ta.e.I % 128 != 0 || ta.e.Is % 128 != 0) return launch_cfg<MODE, CfgMidN>(ta, stream, m);
+        return launch_cfg<MODE, CfgMid>(ta, stream, m);
     default: return launch_cfg<MODE, CfgSmall>(ta, stream, m);
     }
 }
@@ -619,7 +638,7 @@ bool tiled_eligible(int T, int K, int E, int H, int I, int Is, bool bf16)
     // whole k slices (H, I, Is); a gate/up tile takes BN/2 gate channels and
     // the same up channels
     const int which = gu_cfg(T, K, E, Is);
-    const int half = cfg_bn(which == 6 ? 0 : which) / 2;  // CfgWideN falls back to CfgSmall
+    const int half = cfg_bn(which == 6 || which == kTlMid ? 0 : which) / 2;  // CfgWideN, CfgMid fall back to 128-column tiles
     return bf16 && H % 64 == 0 && I % 64 == 0 && Is % 64 == 0 && I % half == 0 && Is % half == 0;
 }
 

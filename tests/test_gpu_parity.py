@@ -62,6 +62,10 @@ SMALL = [
     ("t300",      300, 256, 64, 6, 128, 128, True, False),   # two dispatch tiles, 16-row tiles
     ("t600_f32",  600, 128, 16, 2, 64, 64,  False, False),
     ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
+    ("t700_mid",  700, 256, 128, 4, 128, 128, True, False),  # 64-row gate/up and down tiles
+    ("t600_midg", 600, 256, 64, 4, 128, 256, True, True),    # 64-row gate/up tiles, 128-row down tiles
+    ("t640_midn", 640, 256, 64, 4, 192, 64, True, False),    # 64-row gate/up tiles of 128 columns (widths not whole 256-column tiles)
+    ("t1024_flint", 1024, 2048, 256, 6, 512, 1024, True, False),  # the Flint shape on 64-row gate/up and down tiles
     ("t2100_big", 2100, 256, 16, 4, 128, 128, True, True),   # 256-row tiles, router split over H
     ("t5000_ns",  5000, 128, 8,  2, 128, 0,   True, False),  # 256-row tiles, no shared expert
     # the fused decode kernel (bf16, T <= 64, H and I multiples of 256, Is a multiple of I)
