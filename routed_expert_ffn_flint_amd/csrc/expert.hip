@@ -278,6 +278,16 @@ __device__ __forceinline__ f32x4 combine4(const ExpertArgs &a, int t, int c)
     } else if (a.Is > 0) {
         ys = *reinterpret_cast<const f32x4 *>(a.y_shared + (size_t)t * H + c);
     }
+    // the shared down product's other partial sums, loaded together here and
+    // added in order below (one memory latency for all of them instead of one
+    // each: a dense T = 32 layer's combine of 8 partial arrays 4.6 -> 3.4 us)
+    constexpr int kPre = 8;
+    f32x4 ps[kPre - 1];
+    if (a.Is > 0 && nsplit > 1) {
+#pragma unroll
+        for (int sp = 1; sp < kPre; ++sp)
+            if (sp < nsplit) ps[sp - 1] = *reinterpret_cast<const f32x4 *>(a.y_shared + ((size_t)sp * a.T + t) * H + c);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
@@ -293,7 +303,15 @@ __device__ __forceinline__ f32x4 combine4(const ExpertArgs &a, int t, int c)
         acc[1] += ys[1];
         acc[2] += ys[2];
         acc[3] += ys[3];
-        for (int sp = 1; sp < nsplit; ++sp) {  // the shared down product's other partial sums, in order
+#pragma unroll
+        for (int sp = 1; sp < kPre; ++sp) {
+            if (sp >= nsplit) break;
+            acc[0] += ps[sp - 1][0];
+            acc[1] += ps[sp - 1][1];
+            acc[2] += ps[sp - 1][2];
+            acc[3] += ps[sp - 1][3];
+        }
+        for (int sp = kPre; sp < nsplit; ++sp) {  // (more than kPre partial arrays: the rest one by one)
             const f32x4 v = *reinterpret_cast<const f32x4 *>(a.y_shared + ((size_t)sp * a.T + t) * H + c);
             acc[0] += v[0];
             acc[1] += v[1];
