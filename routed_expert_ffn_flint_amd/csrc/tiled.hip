@@ -589,8 +589,17 @@ int dn_cfg(int T, int K, int E)
     if ((long long)T * K <= (long long)kTlMidDnRows * E) return kTlMid;
     return big_batch(T, K, E) ? kTlDnBig : kTlDnSmall;
 }
-// the 16-row tiles of a MoE layer and the 32-row tiles of a dense layer
+// the 16-row tiles of a MoE layer and the 32-row tiles of a dense layer.
+// The down product leaves the 16-row tiles from kMidDnFromT tokens on where it
+// takes the 64-row ones (T K <= kTlMidDnRows E): Flint shape T = 448 down
+// 119.5 -> 113.6 us, 512 123.1 -> 116.6 (no change at 384; gate/up on 64-row
+// tiles no faster there: 205 -> 208 us at 448).
+constexpr int kMidDnFromT = 448;
 bool moe_small_tiles(int T, int K) { return K > 0 && T < kLargeTilesFromT; }
+bool moe_small_down(int T, int K, int E)
+{
+    return moe_small_tiles(T, K) && (T < kMidDnFromT || dn_cfg(T, K, E) != kTlMid);
+}
 bool dense_small_tiles(int T, int K) { return K == 0 && T < kDenseTiledFromT; }
 
 template <int MODE, typename C>
@@ -674,7 +683,7 @@ int tiled_bm1(int T, int K, int E, int Is)
 }
 int tiled_bm2(int T, int K, int E)
 {
-    if (moe_small_tiles(T, K)) return CfgMoeDn::BM;
+    if (moe_small_down(T, K, E)) return CfgMoeDn::BM;
     if (dense_small_tiles(T, K)) return CfgDecDn::BM;
     return cfg_bm(dn_cfg(T, K, E));
 }
@@ -686,7 +695,9 @@ hipError_t launch_experts_tiled(const ExpertArgs &a, hipStream_t stream, const M
     if (moe_small_tiles(a.T, a.K)) {
         const hipError_t err = launch_cfg<GATE_UP, CfgMoeGu>(ta, stream, marks ? marks[0] : Marks{});
         if (err != hipSuccess) return err;
-        return launch_cfg<DOWN, CfgMoeDn>(ta, stream, marks ? marks[1] : Marks{});
+        const Marks m = marks ? marks[1] : Marks{};
+        return moe_small_down(a.T, a.K, a.E) ? launch_cfg<DOWN, CfgMoeDn>(ta, stream, m)
+                                              : launch_mode<DOWN>(dn_cfg(a.T, a.K, a.E), ta, stream, m);
     }
     if (dense_small_tiles(a.T, a.K)) {
         // a dense layer at decode sizes (layer times measured on the dense layer,

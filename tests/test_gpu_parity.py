@@ -63,6 +63,7 @@ SMALL = [
     ("t600_f32",  600, 128, 16, 2, 64, 64,  False, False),
     ("t1100",     1100, 256, 32, 4, 64, 128, True, True),    # tiled expert kernels, large router
     ("t700_mid",  700, 256, 128, 4, 128, 128, True, False),  # 64-row gate/up and down tiles
+    ("t480_dmid", 480, 256, 128, 4, 128, 128, True, True),   # 16-row gate/up tiles, 64-row down tiles
     ("t600_midg", 600, 256, 64, 4, 128, 256, True, True),    # 64-row gate/up tiles, 128-row down tiles
     ("t640_midn", 640, 256, 64, 4, 192, 64, True, False),    # 64-row gate/up tiles of 128 columns (widths not whole 256-column tiles)
     ("t1024_flint", 1024, 2048, 256, 6, 512, 1024, True, False),  # the Flint shape on 64-row gate/up and down tiles
