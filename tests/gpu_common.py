@@ -99,7 +99,7 @@ def check_routing(gpu_idx, gpu_w, ora_idx, ora_w, near_tie, where="", scores_of=
     Tokens whose GPU set equals the oracle's: weights within WEIGHT_TOL.  A
     token whose set differs must be a near tie (oracle K-th and (K+1)-th scores
     closer than TIE_GAP), and the GPU's set must itself be a correct answer,
-    judged on the oracle's float32 scores (``scores_of(rows)`` returns them,
+    decided on the oracle's float32 scores (``scores_of(rows)`` returns them,
     [len(rows), E]): every selected score at least every unselected one minus
     TIE_GAP; the experts in one set and not the other all within TIE_GAP of the
     oracle's K-th score; and the GPU's weights equal to the scores renormalised
@@ -121,7 +121,7 @@ def check_routing(gpu_idx, gpu_w, ora_idx, ora_w, near_tie, where="", scores_of=
     np.testing.assert_allclose(np.asarray(gpu_w, np.float64).sum(1), 1.0, atol=2e-6)
     rows = np.nonzero(differ)[0]
     if len(rows):
-        assert scores_of is not None, f"{where}: tokens differ; their oracle scores are needed to judge them"
+        assert scores_of is not None, f"{where}: tokens differ; their oracle scores are needed to check them"
         sc = np.asarray(scores_of(rows), np.float64)
         E = sc.shape[1]
         for j, t in enumerate(rows):
